@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of one ZeRO rank's shard optimizer step on one MI355X.
+
+Workload (the graded one): a GPT-2-XL-scale model, psi = 1.5e9 parameters
+split over N = 4 ranks with align 128; rank 0 owns a 375,000,064-parameter
+shard.  fp32 master ~ N(0, 0.02), m ~ N(0, 1e-4), v ~ |N(0, 1e-6)|, one
+pre-reduced fp16 gradient ~ f16(N(0, 1e-3) * 2^16), loss scale 2^16, Adam
+lr 1e-4, betas (0.9, 0.999), eps 1e-8, t = 1000, 1001, ...  All inputs are
+synthetic, seeded, and resident in HBM before timing starts.
+
+One step = the whole hot path on that shard: the partition layout (host),
+the gradient statistics (overflow flag + sum of squares, two kernels) and the
+fused Adam update (one kernel).  ``value`` is shard parameters per second of
+wall time over the K timed steps.  The algorithmic traffic is 30 bytes per
+parameter for the whole call (2 for the statistics pass, 28 for the update).
+
+Also reported: the update kernel alone against the HBM roofline (HIP events
+around each launch, on the launch stream), a plain copy/read kernel as the
+attainable ceiling, the owner-side reduce of 64 fp16 slices of the 7.5B /
+N = 64 shard (117,187,584 parameters), and the CPU oracle timed on a bounded
+sample of the same workload on one host core.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shard Adam step: params/sec and HBM GB/s (% of peak), 1 GPU"
+PEAK_HBM_GBPS = 8000.0
+UPDATE_BYTES_PER_PARAM = 28      # read g2 m4 v4 th4, write m4 v4 th4 p16 2
+STATS_BYTES_PER_PARAM = 2        # read g2
+REDUCE_BYTES_PER_PARAM = lambda n: 2 * n + 4   # noqa: E731
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_update_gpt2xl_shard_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc", f)
+                  for f in ("shard_kernels.hpp", "zero_shard.hip")]
+
+PSI, N_RANKS, RANK, ALIGN = 1_500_000_000, 4, 0, 128
+SEED = 0xC2
+LR, BETAS, EPS, INV_SCALE, T0 = 1e-4, (0.9, 0.999), 1e-8, 2.0 ** -16, 1000
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per update launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken for other kernel code."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def ceiling(torch, tk, dev, n_floats=1 << 30, reps=5):
+    """Plain copy (8 B/element) and read (4 B/element) kernels, GB/s."""
+    src = torch.ones(n_floats, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(1 << 16, dtype=torch.float32, device=dev)
+    out = {}
+    for name, fn, bytes_per in (("copy", lambda: tk.copy_f32(src, dst), 8),
+                                ("read", lambda: tk.read_f32(src, sink), 4)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[f"{name}_gbps"] = round(bytes_per * n_floats * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del src, dst
+    return out
+
+
+def reduce_secondary(torch, zs, tk, dev, steps):
+    """Owner-side reduce of 64 simulated fp16 slices (7.5B model, N = 64)."""
+    lay = zs.partition_layout(7_500_000_000, 64, 0, 128)
+    n = lay.shard_len
+    slices = [tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), 1e-3 * 4096, 0xC3,
+                             tk.STREAM_GRAD + r) for r in range(64)]
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stats = zs.new_stats(dev)
+    ws = zs.new_workspace(n, dev)
+    s = 2.0 ** -12 / 64
+    for _ in range(2):
+        zs.grad_reduce(slices, out, stats=stats, inv_grad_scale=s, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        zs.grad_reduce(slices, out, stats=stats, inv_grad_scale=s, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) * 1e-3 / steps
+    gbps = REDUCE_BYTES_PER_PARAM(64) * n / sec / 1e9
+    del slices
+    return {"workload": "7.5B model at N=64: owner-side sum of 64 fp16 slices of a 117,187,584-param shard "
+                        "into fp32 with fused flag/sum of squares",
+            "ms": round(sec * 1e3, 4), "params_per_s": n / sec, "hbm_gbps": round(gbps, 1),
+            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": REDUCE_BYTES_PER_PARAM(64)}
+
+
+def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
+    """The oracle (single-threaded C, untuned) on the first 2^24 parameters of
+    the shard: statistics then the gated update, repeated until ~10 s."""
+    import numpy as np
+    import oracle
+    n = 1 << 24
+    g_h = g[:n].cpu().view(torch.int16).numpy().view(np.uint16).copy()
+    st = [master[:n].cpu().numpy().copy(), m[:n].cpu().numpy().copy(), v[:n].cpu().numpy().copy(),
+          p16[:n].cpu().view(torch.int16).numpy().view(np.uint16).copy()]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        rc, _, _ = oracle.shard_adam_step(g_h, *st, step=T0 + reps, lr=LR, beta1=BETAS[0], beta2=BETAS[1],
+                                          eps=EPS, inv_scale=INV_SCALE)
+        assert rc == 0
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    cpu_model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n:,} params of the 375,000,064-param shard, statistics + update, "
+                      f"{reps} repetitions in {el:.1f} s",
+            "host_cpu": cpu_model, "host_threads": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one rank's shard step on one GPU; runs on more than one GPU are not "
+              "part of this build (each rank's step is independent, so per-rank throughput is the "
+              "one-GPU figure).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import zero_partitioned_mixed_flat_amd as zs
+    from zero_partitioned_mixed_flat_amd import testkit as tk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lay = zs.partition_layout(PSI, N_RANKS, RANK, ALIGN)
+    L = lay.shard_len
+    log(f"workload: psi={PSI} N={N_RANKS} rank={RANK} shard_len={L}")
+    master, m, v, p16 = tk.init_shard_state(L, SEED, zero_moments=False, device=dev)
+    g = tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 1e-3 * 65536, SEED, tk.STREAM_GRAD)
+    stats = zs.new_stats(dev)
+    ws = zs.new_workspace(L, dev)
+    torch.cuda.synchronize()
+
+    ceil = ceiling(torch, tk, dev)
+    log(f"ceiling: {ceil}")
+
+    def one_step(t, ev=None):
+        layout = zs.partition_layout(PSI, N_RANKS, RANK, ALIGN)          # a1 (host)
+        assert layout.shard_len == L
+        zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)  # a3 (2 kernels)
+        if ev is not None:
+            ev[0].record()
+        zs.adam_step(g, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
+                     stats=stats, stats_precomputed=True)                # a4-a8 (1 kernel)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        one_step(T0 + i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; flag/sumsq = {zs.read_stats(stats)}")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        one_step(T0 + args.warmup + k, evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_s = start.elapsed_time(end) * 1e-3
+    upd_ms = [a.elapsed_time(b) for a, b in evs]
+    upd_avg_s = sum(upd_ms) / len(upd_ms) * 1e-3
+    overflow, sumsq = zs.read_stats(stats)
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, device {dev_s * 1e3:.3f} ms, "
+        f"update avg {upd_avg_s * 1e3:.4f} ms, overflow={overflow}")
+
+    step_s = wall / args.steps
+    value = L / step_s
+    whole_gbps = (UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) * L / step_s / 1e9
+    upd_gbps = UPDATE_BYTES_PER_PARAM * L / upd_avg_s / 1e9
+    traffic = counter_traffic()
+
+    secondary = None
+    if not args.no_secondary:
+        del ws
+        secondary = reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2))
+        log(f"reduce N=64: {secondary}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, g, master, m, v, p16)
+        log(f"cpu baseline: {cpu}")
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "GPT-2-XL-scale shard: psi=1.5e9, N=4, rank 0 owns 375,000,064 params "
+                               "(align 128); fp16 grad N(0,1e-3)*2^16, fp32 master N(0,0.02), m N(0,1e-4), "
+                               "v |N(0,1e-6)|, Adam lr 1e-4 betas (0.9,0.999) eps 1e-8, t from 1000",
+                   "psi": PSI, "n_ranks": N_RANKS, "shard_len": L, "grad_dtype": "f16",
+                   "algorithmic_bytes_per_param": UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM},
+        "hbm_gbps": round(whole_gbps, 1), "hbm_frac_of_peak": round(whole_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"kernel": "adam_update_kernel<f16>", "bound": "hbm", "achieved": round(upd_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(upd_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(upd_avg_s * 1e3, 4),
+                     "algorithmic_bytes_per_launch": UPDATE_BYTES_PER_PARAM * L},
+        "ceiling": ceil,
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * zero_shard.h -- C ABI of the per-rank ZeRO shard optimizer step on one
+ * MI355X (gfx950): the partition of the flat parameter space, the owner-side
+ * gradient reduce, the gradient statistics and the fused mixed-precision Adam
+ * update of one rank's owned partition.
+ *
+ * Sources, cited by page title and section:
+ *   [ZS]  "DeepSpeed ZeRO Stages"
+ *   [S1M] "ZeRO Stage 1 Math"
+ *   [ZOS] "ZeRO Optimization: Stages 1, 2, and 3 Explained"
+ *   [DZE] "DeepSpeed ZeRO: Extreme Memory Efficiency"
+ *
+ * Conventions for every entry point:
+ *   - No exceptions cross the ABI; every call returns a zero_status_t (or a
+ *     size / string as documented).  On failure nothing is enqueued and
+ *     zero_last_error() holds a message for the calling thread.
+ *   - Device pointers are HIP device allocations on the current device and
+ *     must be 16-byte aligned (ZERO_ERR_MISALIGNED otherwise).  Every array
+ *     is owned by the caller; the library never allocates or frees device
+ *     memory and keeps no state between calls (a per-device CU-count cache
+ *     aside).
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns without synchronising; outputs, including
+ *     the device-resident zero_grad_stats_t, are valid once the stream has
+ *     passed that point.
+ *   - Lengths are element counts.  A length of 0 is valid.
+ *   - Floating point: binary32 arithmetic with round-to-nearest-even, no
+ *     contraction, correctly rounded division and square root, subnormals
+ *     kept; fp16 conversion is round-to-nearest-even.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_SHARD_ABI_VERSION 1
+/* Largest number of simulated rank slices one reduce call accepts. */
+#define ZERO_MAX_SLICES 64
+
+typedef enum {
+  ZERO_OK = 0,
+  ZERO_ERR_INVALID_ARG = -1,   /* a null pointer, a bad size or hyperparameter */
+  ZERO_ERR_MISALIGNED = -2,    /* a device pointer not 16-byte aligned */
+  ZERO_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  ZERO_ERR_HIP = -4,           /* a HIP runtime call or launch failed */
+  ZERO_ERR_INT_OVERFLOW = -5   /* a size does not fit in 64 bits */
+} zero_status_t;
+
+typedef enum { ZERO_F16 = 1, ZERO_F32 = 2 } zero_dtype_t;
+
+/* One rank's shard of the flat parameter index space [0, psi). */
+typedef struct {
+  int64_t psi;        /* total number of parameters */
+  int64_t psi_padded; /* n_ranks * shard_len (>= psi) */
+  int64_t shard_len;  /* elements every rank holds, a multiple of align */
+  int64_t offset;     /* first flat index of this rank's shard = rank * shard_len */
+  int64_t real_len;   /* elements of the shard below psi (the rest is padding) */
+} zero_layout_t;
+
+/* Adam hyperparameters, named as in the optimizer block of the DeepSpeed
+ * configuration shown on [DZE] (lr, betas, eps).  No weight decay. */
+typedef struct {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+} zero_adam_hparams_t;
+
+/* Device-resident result of the gradient statistics. */
+typedef struct {
+  uint32_t overflow; /* 1 if any gradient element is +-inf or NaN, else 0 */
+  uint32_t reserved; /* written as 0 */
+  double sumsq;      /* sum over the shard of (f32(x_j) * inv_grad_scale)^2,
+                        accumulated in fp64; unspecified when overflow = 1 */
+} zero_grad_stats_t;
+
+/*
+ * zero_partition_layout -- the disjoint, padded shard of `rank`.
+ * [ZS] section 2 defines the partition (disjoint index sets whose union is
+ * every parameter, each of size about psi/N, owned exclusively by one rank);
+ * [S1M] "The core idea" assigns shard i to rank i; [ZS] section 3.2 keeps the
+ * gradients in one flat contiguous buffer.  Shards are equal contiguous
+ * blocks in rank order: shard_len = ceil(psi / (n_ranks*align)) * align,
+ * offset = rank*shard_len, real_len = clamp(psi - offset, 0, shard_len).
+ * Host arithmetic only.  Errors: out NULL, psi < 0, n_ranks < 1, rank not in
+ * [0, n_ranks), align < 1 or not a power of two -> ZERO_ERR_INVALID_ARG;
+ * n_ranks*align or psi_padded above INT64_MAX -> ZERO_ERR_INT_OVERFLOW.
+ */
+int zero_partition_layout(int64_t psi, int32_t n_ranks, int32_t rank,
+                          int64_t align, zero_layout_t *out);
+
+/*
+ * zero_model_state_bytes -- model-state bytes per GPU for ZeRO stage 0..3
+ * (0 = plain data parallelism) with optimizer multiplier K (12 for
+ * mixed-precision Adam): [ZS] section 1.2 and sections 3.1-3.3; [DZE] "Three
+ * stages of partitioning".  Host arithmetic only.  Errors: out_bytes NULL,
+ * psi < 0, n_ranks < 1, stage not in 0..3, K < 0 -> ZERO_ERR_INVALID_ARG.
+ */
+int zero_model_state_bytes(double psi, int32_t n_ranks, int32_t stage,
+                           double K, double *out_bytes);
+
+/*
+ * zero_workspace_bytes -- bytes of device workspace the statistics of a
+ * shard of `len` elements need (per-block partial results).  A few tens of
+ * KiB at most; the same buffer may be reused by consecutive calls on one
+ * stream.  Returns 0 for len < 0.
+ */
+size_t zero_workspace_bytes(int64_t len);
+
+/*
+ * zero_shard_grad_reduce -- owner-side arithmetic of the gradient
+ * reduce-scatter ([ZS] sections 3.1-3.2: rank i receives the fully reduced
+ * gradient of P_i, reduced into the owner's buffer; [DZE] communication
+ * section: the reduce-scatter sums), for N simulated ranks whose fp16
+ * gradient slices of this shard already sit in this GPU's memory.
+ *   slices          host array of n_slices device pointers, slice r holding
+ *                   `len` fp16 values (binary16 bit patterns) of rank r
+ *   out_sum         device fp32 [len]: out[j] = left fold in fp32 of
+ *                   f32(slice_0[j]) + f32(slice_1[j]) + ... in rank order
+ *   stats           device zero_grad_stats_t or NULL; when given, the
+ *                   overflow flag and sum of squares of (out[j] *
+ *                   inv_grad_scale) are computed in the same pass, so that a
+ *                   following zero_shard_adam_step can skip its own pass
+ *                   (stats_precomputed = 1, same inv_grad_scale)
+ *   inv_grad_scale  multiplier applied to out[j] for the statistics only
+ *   ws, ws_bytes    device workspace of >= zero_workspace_bytes(len) bytes,
+ *                   needed only when stats is not NULL
+ * The sum is not averaged: a caller that wants the mean folds 1/N into
+ * inv_grad_scale.  Errors: n_slices not in [1, ZERO_MAX_SLICES], len < 0,
+ * a NULL slice/out pointer (len > 0), inv_grad_scale not finite or <= 0,
+ * out_sum overlapping a slice -> ZERO_ERR_INVALID_ARG; misaligned pointer ->
+ * ZERO_ERR_MISALIGNED; short workspace -> ZERO_ERR_WORKSPACE.
+ */
+int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices,
+                           int64_t len, float *out_sum,
+                           zero_grad_stats_t *stats, double inv_grad_scale,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * zero_shard_grad_stats -- overflow flag and sum of squares of the shard's
+ * gradient.  [ZS] section 2.1: global clipping needs ||g||_2 over all of P,
+ * one extra scalar all-reduce; this is the shard-local share.  The overflow
+ * check (any +-inf/NaN) is the loss-scaling guard of mixed-precision
+ * training; the pages name mixed precision ([ZS] section 1.2, fp16 enabled
+ * in the configurations of section 8) but do not spell the check out.
+ *   grad       device [len] of fp16 bit patterns (ZERO_F16) or fp32 (ZERO_F32)
+ *   stats      device zero_grad_stats_t, written
+ * Two kernels: per-block partials into `ws`, then one block sums them in a
+ * fixed order (the result is deterministic run to run).  Errors as for the
+ * reduce.
+ */
+int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype,
+                          int64_t len, double inv_grad_scale,
+                          zero_grad_stats_t *stats, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * zero_shard_adam_step -- the local optimizer step of one rank on its owned
+ * shard ([S1M] "The per-step mechanics", beat 3; [ZS] section 2.1 Fact 1:
+ * the update is elementwise, so the shard update is exact on its own).  Per
+ * element, in binary32 ([ZS] section 2.1 equations; [S1M] "Where the 12 bytes
+ * come from"; [ZOS] Stage 2: the shard's gradient is converted to fp32, the
+ * fp32 states and master are updated, the fp16 copy is refreshed):
+ *   g   = f32(grad[j]) * s
+ *   m'  = b1*m + (1-b1)*g              v' = b2*v + (1-b2)*(g*g)
+ *   th' = th - lr * ((m'/(1-b1^t)) / (sqrt(v'/(1-b2^t)) + eps))
+ *   param16[j] = f16(th')
+ * with s = inv_grad_scale and the scalars b1, 1-b1, b2, 1-b2, 1-b1^t, 1-b2^t,
+ * lr, eps, s each computed in double on the host and rounded once to float.
+ *   grad            device [len], fp16 bits or fp32 per grad_dtype (read only)
+ *   master, exp_avg, exp_avg_sq   device fp32 [len], updated in place
+ *   param16         device [len] fp16 bits, written (the shard's slice of the
+ *                   flat compute copy)
+ *   step            t >= 1, the number of this applied step
+ *   hp              host pointer to the hyperparameters
+ *   stats           device zero_grad_stats_t; computed here unless
+ *                   stats_precomputed != 0, in which case it must already
+ *                   hold the statistics of this same gradient and scale
+ *   ws, ws_bytes    device workspace (>= zero_workspace_bytes(len)) when the
+ *                   statistics are computed here; ignored otherwise
+ * Overflow: when stats->overflow is 1 every block exits before touching the
+ * states; master, exp_avg, exp_avg_sq and param16 keep their bits and the
+ * caller should not advance t (the decision never needs a host sync).
+ * Arrays must not overlap one another.  Errors: len < 0, a NULL pointer,
+ * step < 1, lr < 0 or not finite, beta not in [0,1), eps <= 0, inv_grad_scale
+ * not finite or <= 0, overlapping arrays -> ZERO_ERR_INVALID_ARG; misaligned
+ * pointer -> ZERO_ERR_MISALIGNED; short workspace -> ZERO_ERR_WORKSPACE.
+ */
+int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype,
+                         double inv_grad_scale, float *master, float *exp_avg,
+                         float *exp_avg_sq, uint16_t *param16, int64_t len,
+                         int64_t step, const zero_adam_hparams_t *hp,
+                         zero_grad_stats_t *stats, int32_t stats_precomputed,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *zero_status_string(int status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char *zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZERO_SHARD_H */

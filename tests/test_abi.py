@@ -1,0 +1,153 @@
+"""CPU checks of the C ABI: the libraries load, export every function the
+headers declare, and their host-only logic agrees with the oracle.  Calls that
+would reach the GPU are not made here; argument errors are rejected before any
+HIP call, so they are exercised with made-up pointer values."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import zero_partitioned_mixed_flat_amd as zs
+from zero_partitioned_mixed_flat_amd import testkit
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^(?:const\s+)?(?:unsigned\s+)?\w+\s*\*?\s*(zero_\w+)\s*\(", re.M)
+
+
+def _declared(header):
+    return DECL.findall(open(header).read())
+
+
+def test_every_declared_symbol_is_exported():
+    headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert headers
+    libs = {"zero_shard.h": zs.library(), "zero_testkit.h": testkit.library()}
+    for h in headers:
+        names = _declared(h)
+        assert names, h
+        lib = libs[os.path.basename(h)]
+        for name in names:
+            assert hasattr(lib, name), f"{name} declared in {h} but not exported"
+
+
+def test_shard_header_declares_the_path():
+    names = set(_declared(os.path.join(ROOT, "include", "zero_shard.h")))
+    assert {"zero_partition_layout", "zero_model_state_bytes", "zero_workspace_bytes",
+            "zero_shard_grad_reduce", "zero_shard_grad_stats", "zero_shard_adam_step",
+            "zero_status_string", "zero_last_error"} <= names
+
+
+def test_layout_matches_oracle(orc):
+    rng = np.random.default_rng(0)
+    cases = [(psi, n, r, a) for psi in list(range(0, 200)) + [1023, 1024, 1025, 5000]
+             for n in (1, 2, 3, 4, 7, 8, 64) for r in sorted({0, n // 2, n - 1})
+             for a in (1, 4, 128)]
+    cases += [(int(p), int(n), int(rng.integers(0, n)), int(2 ** rng.integers(0, 12)))
+              for p, n in zip(rng.integers(0, 2**40, 2000), rng.integers(1, 1000, 2000))]
+    cases += [(1_048_576, 4, 0, 128), (1_500_000_000, 4, 3, 128), (7_500_000_000, 64, 63, 128),
+              (7_000_000_000, 8, 7, 128), (1_500_000_000, 1, 0, 128)]
+    for psi, n, r, a in cases:
+        st, ref = orc.partition_layout(psi, n, r, a)
+        assert st == 0
+        assert tuple(zs.partition_layout(psi, n, r, a)) == ref, (psi, n, r, a)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((10, 0, 0, 1), -1), ((10, 4, 4, 1), -1), ((10, 4, 0, 3), -1), ((-1, 4, 0, 1), -1),
+    ((2**62, 4, 0, 2**61), -5), ((2**63 - 1, 3, 0, 2**60), -5),
+])
+def test_layout_errors(args, status, orc):
+    with pytest.raises(zs.ZeroError) as e:
+        zs.partition_layout(*args)
+    assert e.value.status == status == orc.partition_layout(*args)[0]
+
+
+def test_model_state_bytes_matches_oracle(orc):
+    for psi in (0.0, 1.5e9, 3e9, 7e9, 7.5e9, 70e9):
+        for n in (1, 4, 8, 64):
+            for stage in range(4):
+                for K in (12.0, 4.0, 6.0):
+                    a = zs.model_state_bytes(psi, n, stage, K)
+                    b = orc.model_state_bytes(psi, n, stage, K)
+                    assert abs(a - b) <= 1e-12 * max(1.0, b)
+    with pytest.raises(zs.ZeroError):
+        zs.model_state_bytes(1e9, 4, 4)
+
+
+def test_workspace_and_status_strings():
+    assert zs.workspace_bytes(0) > 0 and zs.workspace_bytes(10**10) <= 1 << 20
+    assert zs.workspace_bytes(-1) == 0
+    lib = zs.library()
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.zero_status_string(code)
+
+
+def _hp(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8):
+    from zero_partitioned_mixed_flat_amd._native import _HParams
+    return _HParams(lr, b1, b2, eps)
+
+
+A = 1 << 20  # made-up, 16-byte-aligned "device" addresses; never dereferenced
+
+
+def _adam(lib, **kw):
+    a = dict(grad=A, dt=1, s=1.0, master=2 * A, m=3 * A, v=4 * A, p16=5 * A, n=100, step=1,
+             hp=_hp(), stats=6 * A, pre=1, ws=7 * A, wsn=1 << 16)
+    a.update(kw)
+    return lib.zero_shard_adam_step(a["grad"], a["dt"], a["s"], a["master"], a["m"], a["v"], a["p16"], a["n"],
+                                    a["step"], ctypes.byref(a["hp"]) if a["hp"] is not None else None,
+                                    a["stats"], a["pre"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), -1), (dict(dt=3), -1), (dict(grad=None), -1), (dict(master=None), -1),
+    (dict(stats=None), -1), (dict(hp=None), -1), (dict(step=0), -1),
+    (dict(hp=_hp(lr=-1.0)), -1), (dict(hp=_hp(b1=1.0)), -1), (dict(hp=_hp(b2=-0.5)), -1),
+    (dict(hp=_hp(eps=0.0)), -1), (dict(hp=_hp(lr=float("nan"))), -1), (dict(s=0.0), -1),
+    (dict(s=float("inf")), -1), (dict(m=3 * A + 4), -2), (dict(p16=5 * A + 8), -2),
+    (dict(m=2 * A + 64), -1),                       # exp_avg overlaps master
+    (dict(pre=0, ws=None), -1), (dict(pre=0, wsn=16), -3), (dict(pre=0, ws=7 * A + 8), -2),
+])
+def test_adam_step_rejects_bad_arguments(kw, status):
+    lib = zs.library()
+    assert _adam(lib, **kw) == status
+    assert lib.zero_last_error()
+
+
+def test_reduce_and_stats_reject_bad_arguments():
+    lib = zs.library()
+    ptrs = (ctypes.c_void_p * 65)(*[A * (i + 1) for i in range(65)])
+    out = 100 * A
+    f = lib.zero_shard_grad_reduce
+    assert f(ptrs, 0, 10, out, None, 1.0, None, 0, None) == -1          # no slices
+    assert f(ptrs, 65, 10, out, None, 1.0, None, 0, None) == -1         # too many
+    assert f(ptrs, 4, -1, out, None, 1.0, None, 0, None) == -1
+    assert f(ptrs, 4, 10, out, None, 0.0, None, 0, None) == -1          # bad scale
+    assert f(ptrs, 4, 10, out + 4, None, 1.0, None, 0, None) == -2      # misaligned out
+    assert f(ptrs, 4, 10, A, None, 1.0, None, 0, None) == -1            # out overlaps slice 0
+    assert f(ptrs, 4, 10, out, 200 * A, 1.0, None, 0, None) == -1       # stats without workspace
+    assert f(ptrs, 4, 10, out, 200 * A, 1.0, 300 * A, 8, None) == -3    # short workspace
+    bad = (ctypes.c_void_p * 2)(A, A + 2)
+    assert f(bad, 2, 10, out, None, 1.0, None, 0, None) == -2           # misaligned slice
+    g = lib.zero_shard_grad_stats
+    assert g(A, 1, -5, 1.0, 2 * A, 3 * A, 1 << 16, None) == -1
+    assert g(A, 9, 5, 1.0, 2 * A, 3 * A, 1 << 16, None) == -1
+    assert g(A, 1, 5, float("nan"), 2 * A, 3 * A, 1 << 16, None) == -1
+    assert g(A, 1, 5, 1.0, None, 3 * A, 1 << 16, None) == -1
+    assert g(A, 1, 5, 1.0, 2 * A, 3 * A, 16, None) == -3
+    assert g(A + 2, 1, 5, 1.0, 2 * A, 3 * A, 1 << 16, None) == -2
+
+
+def test_philox_known_answers():
+    # Known-answer vectors published with the Random123 Philox4x32-10
+    # reference implementation (Salmon et al., SC'11).
+    kat = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+           ((0xFFFFFFFF,) * 4, (0xFFFFFFFF, 0xFFFFFFFF), (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+           ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+            (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in kat:
+        got = testkit.philox_host(np.array([ctr], dtype=np.uint32), key)[0]
+        assert tuple(int(x) for x in got) == want

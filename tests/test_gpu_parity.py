@@ -1,0 +1,291 @@
+"""GPU parity of the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs, at sizes the oracle finishes in seconds: ragged
+lengths across several tiles, the tiny workload end to end, the reduce for
+N = 1..64, and the invariants (skip on overflow, determinism, separability,
+padding).  The bar: flag bit-exact, fp32 rel <= 1e-6, fp16 <= 1 ulp,
+sum of squares rel <= 1e-10; the expected design result is bit-exact and
+each test also reports the count of inexact elements."""
+import numpy as np
+import pytest
+
+import oracle
+import zero_partitioned_mixed_flat_amd as zs
+from zero_partitioned_mixed_flat_amd import testkit as tk
+from gpu_util import (assert_state_parity, assert_stats, host_f32, host_u16, require_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+LR, BETAS, EPS = 1e-4, (0.9, 0.999), 1e-8
+S16 = 2.0 ** -16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _state(n, seed, zero_moments, dev):
+    return tk.init_shard_state(n, seed, zero_moments=zero_moments, device=dev)
+
+
+def _grad16(n, seed, dev, scale=1e-3 * 65536, stream=tk.STREAM_GRAD):
+    import torch
+    return tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), scale, seed, stream)
+
+
+def _host_state(master, m, v, p16):
+    return [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
+
+
+def _oracle_step(g_host, st, *, step, s):
+    master, m, v, p16 = [a.copy() for a in st]
+    rc, flag, ssq = oracle.shard_adam_step(g_host, master, m, v, p16, step=step, lr=LR, beta1=BETAS[0],
+                                           beta2=BETAS[1], eps=EPS, inv_scale=s)
+    assert rc == 0
+    return (master, m, v, p16), (flag, ssq)
+
+
+def _gpu_step(g, master, m, v, p16, *, step, s, stats=None, precomputed=False):
+    stats = zs.new_stats(g.device) if stats is None else stats
+    zs.adam_step(g, master, m, v, p16, step=step, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s,
+                 stats=stats, stats_precomputed=precomputed)
+    return zs.read_stats(stats)
+
+
+LENGTHS = [1, 3, 4, 5, 7, 255, 256, 1023, 1024, 4095, 4096, 4097, 8191, 65536 + 13, 262_144,
+           1_000_003]
+
+
+@pytest.mark.parametrize("n", LENGTHS)
+@pytest.mark.parametrize("step,zero_moments", [(1, True), (1000, False)])
+def test_step_f16_grad(dev, n, step, zero_moments):
+    seed = 1000 + n
+    say(f"adam_step f16 n={n} step={step} seed={seed}")
+    master, m, v, p16 = _state(n, seed, zero_moments, dev)
+    g = _grad16(n, seed, dev)
+    before = _host_state(master, m, v, p16)
+    g_h = host_u16(g)
+    ref_state, ref_stats = _oracle_step(g_h, before, step=step, s=S16)
+    got_stats = _gpu_step(g, master, m, v, p16, step=step, s=S16)
+    assert_stats(got_stats, ref_stats, f"n={n}")
+    counts = assert_state_parity(_host_state(master, m, v, p16), ref_state, f"n={n}")
+    say("  inexact elements:", counts)
+    assert sum(counts.values()) == 0, "expected bit-exact parity"
+
+
+@pytest.mark.parametrize("n", [1, 6, 4097, 100_003])
+def test_step_f32_grad(dev, n):
+    import torch
+    seed = 2000 + n
+    say(f"adam_step f32 n={n} seed={seed}")
+    master, m, v, p16 = _state(n, seed, False, dev)
+    g = tk.normal_f32_(torch.empty(n, dtype=torch.float32, device=dev), 0.0, 4 * 1e-3 * 65536, seed,
+                       tk.STREAM_GRAD)
+    before = _host_state(master, m, v, p16)
+    ref_state, ref_stats = _oracle_step(host_f32(g), before, step=10, s=2.0 ** -18)
+    got_stats = _gpu_step(g, master, m, v, p16, step=10, s=2.0 ** -18)
+    assert_stats(got_stats, ref_stats, f"f32 n={n}")
+    counts = assert_state_parity(_host_state(master, m, v, p16), ref_state, f"f32 n={n}")
+    assert sum(counts.values()) == 0
+
+
+def test_tiny_workload_end_to_end(dev):
+    """Psi = 1,048,576, N = 4, rank 0 owns 262,144 (align 128); four simulated
+    ranks' fp16 gradients ~ N(0,1e-3)*2^16 are summed on the owner, then one
+    Adam step at t = 1 from m = v = 0 with s = 2^-16/4 (the mean enters
+    through the scale)."""
+    import torch
+    lay = zs.partition_layout(1_048_576, 4, 0, 128)
+    assert tuple(lay) == oracle.partition_layout(1_048_576, 4, 0, 128)[1]
+    n = lay.shard_len
+    assert n == 262_144
+    seed = 0xC1
+    say(f"tiny workload: reduce N=4 + step, n={n}")
+    slices = [_grad16(n, seed, dev, stream=tk.STREAM_GRAD + r) for r in range(4)]
+    master, m, v, p16 = _state(n, seed, True, dev)
+    s = 2.0 ** -16 / 4
+    gsum = torch.empty(n, dtype=torch.float32, device=dev)
+    stats = zs.new_stats(dev)
+    zs.grad_reduce(slices, gsum, stats=stats, inv_grad_scale=s)
+    red_stats = zs.read_stats(stats)
+    before = _host_state(master, m, v, p16)
+    slices_h = [host_u16(t) for t in slices]
+    ref_sum = oracle.grad_reduce(slices_h)
+    assert np.array_equal(host_f32(gsum).view(np.uint32), ref_sum.view(np.uint32))
+    assert_stats(red_stats, oracle.grad_stats(ref_sum, s), "tiny reduce")
+    _gpu_step(gsum, master, m, v, p16, step=1, s=s, stats=stats, precomputed=True)
+    ref_state, _ = _oracle_step(ref_sum, before, step=1, s=s)
+    counts = assert_state_parity(_host_state(master, m, v, p16), ref_state, "tiny")
+    say("  inexact:", counts)
+    assert sum(counts.values()) == 0
+    # t = 1 from m = v = 0: the step is the closed form theta - lr*g/(|g|+eps)
+    g = ref_sum.astype(np.float64) * s
+    closed = before[0].astype(np.float64) - LR * g / (np.abs(g) + EPS)
+    th = host_f32(master).astype(np.float64)
+    assert (np.abs(th - closed) <= np.spacing(np.abs(host_f32(master))) / 2 + 8 * 2.0 ** -24 * LR).all()
+
+
+@pytest.mark.parametrize("n_slices", [1, 2, 3, 8, 9, 17, 64])
+@pytest.mark.parametrize("n", [5, 2048, 2049, 70_001])
+def test_reduce(dev, n_slices, n):
+    import torch
+    seed = 31 * n_slices + n
+    say(f"grad_reduce N={n_slices} n={n} seed={seed}")
+    slices = [_grad16(n, seed, dev, scale=1e-3 * 4096, stream=tk.STREAM_GRAD + r) for r in range(n_slices)]
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stats = zs.new_stats(dev)
+    s = 2.0 ** -12 / n_slices
+    zs.grad_reduce(slices, out, stats=stats, inv_grad_scale=s)
+    ref = oracle.grad_reduce([host_u16(t) for t in slices])
+    assert np.array_equal(host_f32(out).view(np.uint32), ref.view(np.uint32))
+    assert_stats(zs.read_stats(stats), oracle.grad_stats(ref, s), f"reduce N={n_slices}")
+    out2 = torch.empty(n, dtype=torch.float32, device=dev)
+    zs.grad_reduce(slices, out2)            # without statistics
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("special", [np.inf, -np.inf, np.nan])
+def test_reduce_flags_nonfinite_slice(dev, special):
+    import torch
+    n, N = 9000, 5
+    slices = [_grad16(n, 77, dev, stream=tk.STREAM_GRAD + r) for r in range(N)]
+    slices[3][4321] = float(special)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stats = zs.new_stats(dev)
+    zs.grad_reduce(slices, out, stats=stats, inv_grad_scale=2.0 ** -18)
+    ref = oracle.grad_reduce([host_u16(t) for t in slices])
+    got = host_f32(out)
+    keep = np.ones(n, dtype=bool)
+    keep[4321] = False
+    assert np.array_equal(got.view(np.uint32)[keep], ref.view(np.uint32)[keep])
+    assert np.isnan(got[4321]) == np.isnan(ref[4321]) and (np.isnan(ref[4321]) or got[4321] == ref[4321])
+    assert zs.read_stats(stats)[0] == 1 == oracle.grad_stats(ref, 2.0 ** -18)[0]
+
+
+@pytest.mark.parametrize("special,pos", [(np.inf, 0), (-np.inf, 131_071), (np.nan, 77_777)])
+def test_overflow_skips_step(dev, special, pos):
+    n = 131_072
+    master, m, v, p16 = _state(n, 5, False, dev)
+    g = _grad16(n, 5, dev)
+    g[pos] = float(special)
+    before = _host_state(master, m, v, p16)
+    flag, _ = _gpu_step(g, master, m, v, p16, step=3, s=S16)
+    ref_state, (ref_flag, _) = _oracle_step(host_u16(g), before, step=3, s=S16)
+    assert flag == ref_flag == 1
+    after = _host_state(master, m, v, p16)
+    for a, b in zip(after, before):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_inf_injection_run(dev):
+    n = 500_000
+    g = _grad16(n, 0xC4, dev)
+    tk.inject_inf_f16_(g, 1e-5, 0xC4F)
+    g_h = host_u16(g)
+    n_inf = int((g_h == 0x7C00).sum())
+    say(f"injected +inf count: {n_inf}")
+    master, m, v, p16 = _state(n, 0xC4, False, dev)
+    before = _host_state(master, m, v, p16)
+    flag, _ = _gpu_step(g, master, m, v, p16, step=1000, s=S16)
+    assert flag == oracle.grad_stats(g_h, S16)[0] == (1 if n_inf else 0)
+    if n_inf:
+        for a, b in zip(_host_state(master, m, v, p16), before):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_deterministic(dev):
+    import torch
+    n = 300_001
+    outs = []
+    for _ in range(2):
+        master, m, v, p16 = _state(n, 42, False, dev)
+        g = _grad16(n, 42, dev)
+        st = _gpu_step(g, master, m, v, p16, step=17, s=S16)
+        outs.append((st, [t.clone() for t in (master, m, v, p16)]))
+    assert outs[0][0] == outs[1][0]            # flag and sumsq bit-identical
+    for a, b in zip(outs[0][1], outs[1][1]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_sharded_equals_unsharded(dev):
+    """Fact 1 of "DeepSpeed ZeRO Stages" 2.1: updating shards separately is
+    exactly the update of the whole; the shard views come from the layout."""
+    import torch
+    psi, N = 1_000_000, 4
+    lay = [zs.partition_layout(psi, N, r, 128) for r in range(N)]
+    total = lay[0].psi_padded
+    master, m, v, p16 = _state(total, 9, False, dev)
+    g = _grad16(total, 9, dev)
+    whole = [t.clone() for t in (master, m, v, p16)]
+    _gpu_step(g, *whole, step=5, s=S16)
+    for L in lay:
+        sl = slice(L.offset, L.offset + L.shard_len)
+        _gpu_step(g[sl], master[sl], m[sl], v[sl], p16[sl], step=5, s=S16)
+    for a, b in zip((master, m, v, p16), whole):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_padding_stays_zero(dev):
+    import torch
+    lay = zs.partition_layout(1_500_001, 4, 3, 128)
+    n, real = lay.shard_len, lay.real_len
+    assert n > real
+    master, m, v, p16 = _state(n, 3, False, dev)
+    g = _grad16(n, 3, dev)
+    for t in (master, m, v, p16, g):
+        t[real:] = 0
+    _gpu_step(g, master, m, v, p16, step=2, s=S16)
+    for t in (master, m, v, p16):
+        assert not t[real:].view(torch.uint8).any()
+
+
+def test_zero_length(dev):
+    import torch
+    e32 = torch.empty(0, dtype=torch.float32, device=dev)
+    e16 = torch.empty(0, dtype=torch.float16, device=dev)
+    stats = zs.new_stats(dev)
+    stats.fill_(0xFF)
+    zs.adam_step(e16, e32, e32.clone(), e32.clone(), e16.clone(), step=1, lr=LR, stats=stats)
+    assert zs.read_stats(stats) == (0, 0.0)
+    stats.fill_(0xFF)
+    zs.grad_reduce([e16, e16.clone()], e32.clone(), stats=stats)
+    assert zs.read_stats(stats) == (0, 0.0)
+
+
+def test_misaligned_view_is_rejected(dev):
+    import torch
+    master, m, v, p16 = _state(64, 1, False, dev)
+    g = _grad16(64, 1, dev)
+    with pytest.raises(zs.ZeroError) as e:
+        _gpu_step(g[1:], master[1:], m[1:], v[1:], p16[1:], step=1, s=S16)
+    assert e.value.status == -2
+    with pytest.raises(zs.ZeroError):
+        _gpu_step(g, master, m, v, p16, step=0, s=S16)
+    out = torch.empty(63, dtype=torch.float32, device=dev)
+    with pytest.raises(zs.ZeroError):
+        zs.grad_reduce([g[1:]], out)
+
+
+def test_generator_matches_host_philox(dev):
+    n = 4096
+    got = tk.philox(n, 0x1234_5678_9ABC_DEF0, 7).cpu().numpy().view(np.uint32).reshape(n, 4)
+    ctr = np.zeros((n, 4), dtype=np.uint32)
+    ctr[:, 0] = np.arange(n, dtype=np.uint32)
+    ctr[:, 2] = 7
+    ref = tk.philox_host(ctr, (0x9ABC_DEF0, 0x1234_5678))
+    assert np.array_equal(got, ref)
+
+
+def test_generator_moments(dev):
+    import torch
+    n = 1 << 22
+    x = tk.normal_f32_(torch.empty(n, dtype=torch.float32, device=dev), 0.0, 1.0, 11, 1).double().cpu().numpy()
+    se = 1 / np.sqrt(n)
+    assert abs(x.mean()) < 5 * se and abs(x.std() - 1) < 5 * se
+    from scipy.stats import t as student_t
+    t3 = tk.student_t3_f16_(torch.empty(n, dtype=torch.float16, device=dev), scale=1.0, seed=12, stream=2)
+    t3 = t3.float().cpu().numpy().astype(np.float64)
+    # tail mass beyond 2 of Student-t with 3 degrees of freedom, from scipy
+    want = 2 * student_t.sf(2.0, 3)
+    p = (np.abs(t3) > 2).mean()
+    assert abs(p - want) < 5 * np.sqrt(want * (1 - want) / n)

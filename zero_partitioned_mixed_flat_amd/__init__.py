@@ -1,0 +1,24 @@
+"""MI355X-native per-rank ZeRO shard optimizer step.
+
+One data-parallel rank's share of ZeRO-partitioned mixed-precision training
+(the pages "DeepSpeed ZeRO Stages", "ZeRO Stage 1 Math", "ZeRO Optimization:
+Stages 1, 2, and 3 Explained", "DeepSpeed ZeRO: Extreme Memory Efficiency"):
+
+* ``partition_layout``  -- the rank's disjoint, padded shard of the flat space
+* ``grad_reduce``       -- owner-side fp32 sum of N fp16 gradient slices
+* ``grad_stats``        -- overflow flag and sum of squares of the gradient
+* ``adam_step``         -- fused fp32 Adam update of master/m/v + fp16 copy
+
+All device work runs in the HIP library ``libzero_shard.so`` (C ABI in
+``include/zero_shard.h``); this package only marshals arguments.
+"""
+from ._native import (  # noqa: F401
+    STATS_BYTES, ZERO_F16, ZERO_F32, ZERO_MAX_SLICES, Layout, ZeroError, adam_step,
+    grad_reduce, grad_stats, library, model_state_bytes, new_stats, new_workspace,
+    partition_layout, read_stats, workspace_bytes)
+
+__all__ = [
+    "Layout", "ZeroError", "partition_layout", "model_state_bytes", "workspace_bytes",
+    "new_workspace", "new_stats", "read_stats", "grad_reduce", "grad_stats", "adam_step",
+    "library", "ZERO_F16", "ZERO_F32", "ZERO_MAX_SLICES", "STATS_BYTES",
+]

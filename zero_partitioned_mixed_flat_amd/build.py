@@ -1,0 +1,63 @@
+"""Build the package's HIP libraries in-tree for gfx950 with hipcc.
+
+``libzero_shard.so``   the C ABI of include/zero_shard.h (the optimizer step)
+``libzero_testkit.so`` seeded synthetic inputs and streaming reference kernels
+                       (include/zero_testkit.h), used by tests and benchmarks
+
+Flags: no FMA contraction, no fast-math (IEEE division and square root stay
+correctly rounded), and packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+CSRC = os.path.join(PKG, "csrc")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+LIBS = {
+    "libzero_shard.so": ["zero_shard.hip"],
+    "libzero_testkit.so": ["testkit.hip"],
+}
+
+
+def library_path(name: str) -> str:
+    return os.path.join(PKG, name)
+
+
+def build_library(name: str, extra_flags=(), out_path: str | None = None, verbose=False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in LIBS[name]]
+    out = out_path or library_path(name)
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *HIP_FLAGS, *extra_flags, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed building {name}")
+    os.replace(tmp, out)
+    return out
+
+
+def build_all(verbose=False) -> list[str]:
+    return [build_library(name, verbose=verbose) for name in LIBS]
+
+
+if __name__ == "__main__":
+    for p in build_all(verbose=True):
+        print("built", p)

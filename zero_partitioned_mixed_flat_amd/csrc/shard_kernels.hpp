@@ -1,0 +1,380 @@
+// shard_kernels.hpp -- gfx950 kernels of the per-rank ZeRO shard optimizer
+// step.  Every kernel is elementwise and bound by HBM bandwidth ("DeepSpeed
+// ZeRO Stages" section 5.1: the step is O(1) arithmetic per parameter and
+// touches the optimizer state once), so none uses MFMA; the design is about
+// bytes in flight and access shape:
+//   * blocks of 256 threads = four wave64s;
+//   * each lane handles chunks of 4 consecutive elements, so one wave's
+//     access to an fp32 stream is one contiguous 1 KiB (16 B per lane) and to
+//     an fp16 stream one contiguous 512 B (8 B per lane);
+//   * U chunks per lane are loaded before any is used, to keep enough loads
+//     outstanding per CU to cover HBM latency;
+//   * grid-stride loops over tiles, with the grid sized from the CU count;
+//   * reductions of the statistics: per-lane fp64 accumulation, butterfly
+//     shuffles inside the wave, LDS across the four waves, one partial per
+//     block, then a single-block pass over the partials in index order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_shard.h"
+
+namespace zs {
+
+constexpr int kBlock = 256;  // threads per block
+constexpr int kWave = 64;    // CDNA wavefront width
+constexpr int kChunk = 4;    // consecutive elements per lane per access
+constexpr int kMaxPartials = 2048;
+
+// Per-step constants, each derived in double on the host and rounded once.
+struct StepScalars {
+  float b1, omb1, b2, omb2, bc1, bc2, lr, eps, s;
+};
+
+// One block's share of the statistics.
+struct Partial {
+  double sumsq;
+  uint32_t flag;
+  uint32_t pad;
+};
+
+struct SliceTable {
+  const uint16_t *p[ZERO_MAX_SLICES];
+};
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+  // binary32 -> binary16 with the hardware conversion: round to nearest
+  // even (the default mode), overflow to inf, subnormals kept.
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+
+__device__ __forceinline__ bool nonfinite_f32(float x) {
+  return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u;
+}
+
+// A packed pair of binary16 codes has an all-ones exponent in either half.
+__device__ __forceinline__ uint32_t nonfinite_f16x2(uint32_t w) {
+  return static_cast<uint32_t>((w & 0x7C00u) == 0x7C00u) |
+         static_cast<uint32_t>((w & 0x7C000000u) == 0x7C000000u);
+}
+
+// The Adam update of one element ("DeepSpeed ZeRO Stages" 2.1 equations;
+// "ZeRO Stage 1 Math", "Where the 12 bytes come from"): one IEEE binary32
+// operation per operator in the order written, nothing fused.
+__device__ __forceinline__ void adam_element(float x, float &m, float &v, float &th,
+                                             uint32_t &p16, const StepScalars &c) {
+#pragma clang fp contract(off)
+  const float g = x * c.s;
+  const float m1 = c.b1 * m + c.omb1 * g;
+  const float v1 = c.b2 * v + c.omb2 * (g * g);
+  const float mh = m1 / c.bc1;
+  const float vh = v1 / c.bc2;
+  const float th1 = th - c.lr * (mh / (__builtin_sqrtf(vh) + c.eps));
+  m = m1;
+  v = v1;
+  th = th1;
+  p16 = f2h(th1);
+}
+
+// Sum of a double and OR of a flag over the block; thread 0 stores them.
+__device__ __forceinline__ void block_partial(double ssq, uint32_t flag, Partial *out) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    ssq += __shfl_xor(ssq, off, kWave);
+    flag |= __shfl_xor(flag, off, kWave);
+  }
+  __shared__ double s_ssq[kBlock / kWave];
+  __shared__ uint32_t s_flag[kBlock / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  if (lane == 0) {
+    s_ssq[wave] = ssq;
+    s_flag[wave] = flag;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = s_ssq[0];
+    uint32_t f = s_flag[0];
+#pragma unroll
+    for (int w = 1; w < kBlock / kWave; ++w) {
+      t += s_ssq[w];
+      f |= s_flag[w];
+    }
+    out->sumsq = t;
+    out->flag = f;
+    out->pad = 0u;
+  }
+}
+
+// Adds (x*s)^2 in double; the product x*s is the binary32 unscaled gradient
+// the update sees, and its square is exact in double.
+__device__ __forceinline__ double sq_unscaled(float x, float s) {
+#pragma clang fp contract(off)
+  const double d = static_cast<double>(x * s);
+  return d * d;
+}
+
+// ---------------------------------------------------------------- statistics
+// Pass 1 of the statistics: per-block flag and sum of squares.
+template <zero_dtype_t DT, int U>
+__global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restrict__ grad,
+                                                            int64_t len, float s,
+                                                            Partial *__restrict__ partials) {
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kChunk * U;
+  const int64_t ntiles = (len + kTile - 1) / kTile;
+  double acc0 = 0.0, acc1 = 0.0;
+  uint32_t flag = 0u;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t base = tile * kTile;
+    if (base + kTile <= len) {
+      if constexpr (DT == ZERO_F16) {
+        const uint16_t *g = static_cast<const uint16_t *>(grad);
+        uint2 raw[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+          raw[k] = *reinterpret_cast<const uint2 *>(g + base + k * (kBlock * kChunk) + threadIdx.x * kChunk);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          flag |= nonfinite_f16x2(raw[k].x) | nonfinite_f16x2(raw[k].y);
+          acc0 += sq_unscaled(h2f(raw[k].x & 0xFFFFu), s);
+          acc1 += sq_unscaled(h2f(raw[k].x >> 16), s);
+          acc0 += sq_unscaled(h2f(raw[k].y & 0xFFFFu), s);
+          acc1 += sq_unscaled(h2f(raw[k].y >> 16), s);
+        }
+      } else {
+        const float *g = static_cast<const float *>(grad);
+        float4 raw[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+          raw[k] = *reinterpret_cast<const float4 *>(g + base + k * (kBlock * kChunk) + threadIdx.x * kChunk);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          flag |= static_cast<uint32_t>(nonfinite_f32(raw[k].x) | nonfinite_f32(raw[k].y) |
+                                        nonfinite_f32(raw[k].z) | nonfinite_f32(raw[k].w));
+          acc0 += sq_unscaled(raw[k].x, s);
+          acc1 += sq_unscaled(raw[k].y, s);
+          acc0 += sq_unscaled(raw[k].z, s);
+          acc1 += sq_unscaled(raw[k].w, s);
+        }
+      }
+    } else {
+      // the ragged last tile, element by element
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+          const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk + e;
+          if (j < len) {
+            float x;
+            if constexpr (DT == ZERO_F16) {
+              const uint32_t h = static_cast<const uint16_t *>(grad)[j];
+              flag |= static_cast<uint32_t>((h & 0x7C00u) == 0x7C00u);
+              x = h2f(h);
+            } else {
+              x = static_cast<const float *>(grad)[j];
+              flag |= static_cast<uint32_t>(nonfinite_f32(x));
+            }
+            acc0 += sq_unscaled(x, s);
+          }
+        }
+      }
+    }
+  }
+  block_partial(acc0 + acc1, flag, &partials[blockIdx.x]);
+}
+
+// Pass 2: one block folds the partials in a fixed order.
+__global__ __launch_bounds__(kBlock) void finalize_stats_kernel(const Partial *__restrict__ partials,
+                                                                int nparts,
+                                                                zero_grad_stats_t *__restrict__ stats) {
+  double ssq = 0.0;
+  uint32_t flag = 0u;
+  for (int i = threadIdx.x; i < nparts; i += kBlock) {
+    ssq += partials[i].sumsq;
+    flag |= partials[i].flag;
+  }
+  __shared__ Partial total;
+  block_partial(ssq, flag, &total);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    stats->overflow = total.flag != 0u ? 1u : 0u;
+    stats->reserved = 0u;
+    stats->sumsq = total.sumsq;
+  }
+}
+
+// -------------------------------------------------------------------- reduce
+// Owner-side reduce of N fp16 slices into fp32, left fold in rank order,
+// optionally with the statistics of (sum * s) in the same pass.  Slices are
+// read G at a time so G*U loads are in flight before the in-order adds.
+template <bool WITH_STATS, int U, int G>
+__global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int n, int64_t len,
+                                                             float *__restrict__ out, float s,
+                                                             Partial *__restrict__ partials) {
+#pragma clang fp contract(off)
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kChunk * U;
+  const int64_t ntiles = (len + kTile - 1) / kTile;
+  double acc0 = 0.0, acc1 = 0.0;
+  uint32_t flag = 0u;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t base = tile * kTile;
+    if (base + kTile <= len) {
+      float acc[U][kChunk];
+      {
+        uint2 raw[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+          raw[k] = *reinterpret_cast<const uint2 *>(tab.p[0] + base + k * (kBlock * kChunk) + threadIdx.x * kChunk);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          acc[k][0] = h2f(raw[k].x & 0xFFFFu);
+          acc[k][1] = h2f(raw[k].x >> 16);
+          acc[k][2] = h2f(raw[k].y & 0xFFFFu);
+          acc[k][3] = h2f(raw[k].y >> 16);
+        }
+      }
+      for (int r0 = 1; r0 < n; r0 += G) {
+        const int cnt = (n - r0) < G ? (n - r0) : G;
+        uint2 raw[G][U];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          if (q < cnt) {
+            const uint16_t *p = tab.p[r0 + q];
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+              raw[q][k] = *reinterpret_cast<const uint2 *>(p + base + k * (kBlock * kChunk) + threadIdx.x * kChunk);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          if (q < cnt) {
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+              acc[k][0] = acc[k][0] + h2f(raw[q][k].x & 0xFFFFu);
+              acc[k][1] = acc[k][1] + h2f(raw[q][k].x >> 16);
+              acc[k][2] = acc[k][2] + h2f(raw[q][k].y & 0xFFFFu);
+              acc[k][3] = acc[k][3] + h2f(raw[q][k].y >> 16);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk;
+        *reinterpret_cast<float4 *>(out + j) = make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
+        if constexpr (WITH_STATS) {
+#pragma unroll
+          for (int e = 0; e < kChunk; ++e) {
+            flag |= static_cast<uint32_t>(nonfinite_f32(acc[k][e]));
+            if (e & 1)
+              acc1 += sq_unscaled(acc[k][e], s);
+            else
+              acc0 += sq_unscaled(acc[k][e], s);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+          const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk + e;
+          if (j < len) {
+            float a = h2f(tab.p[0][j]);
+            for (int r = 1; r < n; ++r) a = a + h2f(tab.p[r][j]);
+            out[j] = a;
+            if constexpr (WITH_STATS) {
+              flag |= static_cast<uint32_t>(nonfinite_f32(a));
+              acc0 += sq_unscaled(a, s);
+            }
+          }
+        }
+      }
+    }
+  }
+  if constexpr (WITH_STATS) block_partial(acc0 + acc1, flag, &partials[blockIdx.x]);
+}
+
+// ---------------------------------------------------------------- the update
+// Fused single pass over the shard: read g, m, v, master; write m, v, master
+// and the fp16 copy (28 B per parameter with an fp16 gradient, 30 B with
+// fp32).  Every block first reads the device-resident overflow flag and
+// leaves before any memory access to the states if it is set.
+template <zero_dtype_t DT, int U>
+__global__ __launch_bounds__(kBlock) void adam_update_kernel(
+    const void *__restrict__ grad, float *__restrict__ master, float *__restrict__ m,
+    float *__restrict__ v, uint16_t *__restrict__ p16, int64_t len, StepScalars c,
+    const zero_grad_stats_t *__restrict__ stats) {
+  if (stats->overflow != 0u) return;
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kChunk * U;
+  const int64_t ntiles = (len + kTile - 1) / kTile;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t base = tile * kTile;
+    if (base + kTile <= len) {
+      float x[U][kChunk];
+      float4 mm[U], vv[U], tt[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk;
+        if constexpr (DT == ZERO_F16) {
+          const uint2 raw = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(grad) + j);
+          x[k][0] = h2f(raw.x & 0xFFFFu);
+          x[k][1] = h2f(raw.x >> 16);
+          x[k][2] = h2f(raw.y & 0xFFFFu);
+          x[k][3] = h2f(raw.y >> 16);
+        } else {
+          const float4 raw = *reinterpret_cast<const float4 *>(static_cast<const float *>(grad) + j);
+          x[k][0] = raw.x;
+          x[k][1] = raw.y;
+          x[k][2] = raw.z;
+          x[k][3] = raw.w;
+        }
+        mm[k] = *reinterpret_cast<const float4 *>(m + j);
+        vv[k] = *reinterpret_cast<const float4 *>(v + j);
+        tt[k] = *reinterpret_cast<const float4 *>(master + j);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        uint32_t h0, h1, h2, h3;
+        adam_element(x[k][0], mm[k].x, vv[k].x, tt[k].x, h0, c);
+        adam_element(x[k][1], mm[k].y, vv[k].y, tt[k].y, h1, c);
+        adam_element(x[k][2], mm[k].z, vv[k].z, tt[k].z, h2, c);
+        adam_element(x[k][3], mm[k].w, vv[k].w, tt[k].w, h3, c);
+        const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk;
+        *reinterpret_cast<float4 *>(m + j) = mm[k];
+        *reinterpret_cast<float4 *>(v + j) = vv[k];
+        *reinterpret_cast<float4 *>(master + j) = tt[k];
+        *reinterpret_cast<uint2 *>(p16 + j) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+          const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk + e;
+          if (j < len) {
+            float x;
+            if constexpr (DT == ZERO_F16)
+              x = h2f(static_cast<const uint16_t *>(grad)[j]);
+            else
+              x = static_cast<const float *>(grad)[j];
+            float mj = m[j], vj = v[j], tj = master[j];
+            uint32_t h;
+            adam_element(x, mj, vj, tj, h, c);
+            m[j] = mj;
+            v[j] = vj;
+            master[j] = tj;
+            p16[j] = static_cast<uint16_t>(h);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace zs

@@ -1,0 +1,242 @@
+// testkit.hip -- seeded synthetic inputs (Philox4x32-10 + Box-Muller) and
+// plain streaming reference kernels; see include/zero_testkit.h.  None of
+// this is part of the optimizer step.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+
+#include "zero_testkit.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64-bit
+// multiplies with the Weyl key schedule.
+__device__ __forceinline__ U4 philox(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c.x;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+    const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+    const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
+    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+__device__ __forceinline__ U4 draw(uint64_t seed, uint32_t stream, int64_t j, uint32_t d) {
+  const uint64_t uj = static_cast<uint64_t>(j);
+  return philox(U4{static_cast<uint32_t>(uj), static_cast<uint32_t>(uj >> 32), stream, d},
+                static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+}
+
+__device__ __forceinline__ double unit53(uint32_t a, uint32_t b) {
+  return (static_cast<double>(a >> 5) * 67108864.0 + static_cast<double>(b >> 6) + 0.5) *
+         1.1102230246251565404e-16;  // 2^-53
+}
+
+// Both Box-Muller normals of one Philox block.
+__device__ __forceinline__ void normals(U4 w, double &z0, double &z1) {
+  const double u1 = unit53(w.x, w.y), u2 = unit53(w.z, w.w);
+  const double r = sqrt(-2.0 * log(u1));
+  const double a = 6.283185307179586476925 * u2;
+  z0 = r * cos(a);
+  z1 = r * sin(a);
+}
+
+__device__ __forceinline__ uint16_t to_half_bits(double x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(x)));
+}
+
+__global__ void philox_kernel(uint32_t *out, int64_t n, uint64_t seed, uint32_t stream) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    const U4 w = draw(seed, stream, i, 0u);
+    out[4 * i + 0] = w.x;
+    out[4 * i + 1] = w.y;
+    out[4 * i + 2] = w.z;
+    out[4 * i + 3] = w.w;
+  }
+}
+
+__global__ void normal_f32_kernel(float *out, int64_t n, double mean, double std, int abs_value,
+                                  uint64_t seed, uint32_t stream) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * kBlock) {
+    double z0, z1;
+    normals(draw(seed, stream, j, 0u), z0, z1);
+    double x = mean + std * z0;
+    if (abs_value) x = fabs(x);
+    out[j] = static_cast<float>(x);
+  }
+}
+
+__global__ void normal_f16_kernel(uint16_t *out, int64_t n, double scale, uint64_t seed, uint32_t stream) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * kBlock) {
+    double z0, z1;
+    normals(draw(seed, stream, j, 0u), z0, z1);
+    out[j] = to_half_bits(scale * z0);
+  }
+}
+
+__global__ void student_t3_f16_kernel(uint16_t *out, int64_t n, double scale, int redraw, uint64_t seed,
+                                      uint32_t stream) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * kBlock) {
+    uint16_t h = 0;
+    const int attempts = redraw ? 8 : 1;
+    for (int a = 0; a < attempts; ++a) {
+      double z0, z1, z2, z3;
+      normals(draw(seed, stream, j, 2u * a), z0, z1);
+      normals(draw(seed, stream, j, 2u * a + 1u), z2, z3);
+      const double t = z0 / sqrt((z1 * z1 + z2 * z2 + z3 * z3) / 3.0);
+      h = to_half_bits(scale * t);
+      if ((h & 0x7C00u) != 0x7C00u) break;
+      if (redraw && a == attempts - 1) h = static_cast<uint16_t>((h & 0x8000u) | 0x7BFFu);
+    }
+    out[j] = h;
+  }
+}
+
+__global__ void inject_inf_kernel(uint16_t *out, int64_t n, double prob, uint64_t seed, uint32_t stream) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * kBlock) {
+    const U4 w = draw(seed, stream, j, 0u);
+    if (unit53(w.x, w.y) < prob) out[j] = 0x7C00u;
+  }
+}
+
+__global__ void copy_f32_kernel(const float4 *__restrict__ src, float4 *__restrict__ dst, int64_t n4,
+                                const float *__restrict__ src_tail, float *__restrict__ dst_tail, int tail) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+  if (blockIdx.x == 0 && threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
+}
+
+__global__ void read_f32_kernel(const float4 *__restrict__ src, int64_t n4, float *__restrict__ sink,
+                                int sink_len) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  float acc = 0.f;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n4; i += stride) {
+    const float4 x = src[i];
+    acc += x.x + x.y + x.z + x.w;
+  }
+  __shared__ float s[kBlock];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = kBlock / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && blockIdx.x < sink_len) sink[blockIdx.x] = s[0];
+}
+
+int grid_for(int64_t n) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0) cus = c;
+  }
+  const int64_t need = (n + kBlock - 1) / kBlock;
+  const int64_t cap = static_cast<int64_t>(cus) * 8;
+  const int64_t g = need < cap ? need : cap;
+  return static_cast<int>(g < 1 ? 1 : g);
+}
+
+thread_local char g_err[256] = "";
+
+// Drops an error left by an earlier, unrelated HIP call on this thread.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int launched() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return 0;
+  std::snprintf(g_err, sizeof g_err, "%s", hipGetErrorString(e));
+  return -4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_testkit_philox(uint32_t *out, int64_t n_blocks, uint64_t seed, uint32_t stream, hipStream_t stream_) {
+  if (n_blocks < 0 || (n_blocks > 0 && out == nullptr)) return -1;
+  if (n_blocks == 0) return 0;
+  clear_stale_error();
+  philox_kernel<<<grid_for(n_blocks), kBlock, 0, stream_>>>(out, n_blocks, seed, stream);
+  return launched();
+}
+
+int zero_testkit_normal_f32(float *out, int64_t n, double mean, double std, int32_t abs_value, uint64_t seed,
+                            uint32_t stream, hipStream_t stream_) {
+  if (n < 0 || (n > 0 && out == nullptr) || !std::isfinite(mean) || !std::isfinite(std)) return -1;
+  if (n == 0) return 0;
+  clear_stale_error();
+  normal_f32_kernel<<<grid_for(n), kBlock, 0, stream_>>>(out, n, mean, std, abs_value, seed, stream);
+  return launched();
+}
+
+int zero_testkit_normal_f16(uint16_t *out, int64_t n, double scale, uint64_t seed, uint32_t stream,
+                            hipStream_t stream_) {
+  if (n < 0 || (n > 0 && out == nullptr) || !std::isfinite(scale)) return -1;
+  if (n == 0) return 0;
+  clear_stale_error();
+  normal_f16_kernel<<<grid_for(n), kBlock, 0, stream_>>>(out, n, scale, seed, stream);
+  return launched();
+}
+
+int zero_testkit_student_t3_f16(uint16_t *out, int64_t n, double scale, int32_t redraw_overflow, uint64_t seed,
+                                uint32_t stream, hipStream_t stream_) {
+  if (n < 0 || (n > 0 && out == nullptr) || !std::isfinite(scale)) return -1;
+  if (n == 0) return 0;
+  clear_stale_error();
+  student_t3_f16_kernel<<<grid_for(n), kBlock, 0, stream_>>>(out, n, scale, redraw_overflow, seed, stream);
+  return launched();
+}
+
+int zero_testkit_inject_inf_f16(uint16_t *out, int64_t n, double prob, uint64_t seed, uint32_t stream,
+                                hipStream_t stream_) {
+  if (n < 0 || (n > 0 && out == nullptr) || !(prob >= 0.0 && prob <= 1.0)) return -1;
+  if (n == 0) return 0;
+  clear_stale_error();
+  inject_inf_kernel<<<grid_for(n), kBlock, 0, stream_>>>(out, n, prob, seed, stream);
+  return launched();
+}
+
+int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream_) {
+  if (n < 0 || (n > 0 && (src == nullptr || dst == nullptr))) return -1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return -1;
+  if (n == 0) return 0;
+  const int64_t n4 = n / 4;
+  const int tail = static_cast<int>(n - n4 * 4);
+  clear_stale_error();
+  copy_f32_kernel<<<grid_for(n4 > 0 ? n4 : 1), kBlock, 0, stream_>>>(
+      reinterpret_cast<const float4 *>(src), reinterpret_cast<float4 *>(dst), n4, src + n4 * 4, dst + n4 * 4, tail);
+  return launched();
+}
+
+int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len, hipStream_t stream_) {
+  if (n < 0 || sink_len < 1 || sink == nullptr || (n > 0 && src == nullptr)) return -1;
+  if (reinterpret_cast<uintptr_t>(src) & 15u) return -1;
+  const int64_t n4 = n / 4;
+  clear_stale_error();
+  read_f32_kernel<<<grid_for(n4 > 0 ? n4 : 1), kBlock, 0, stream_>>>(reinterpret_cast<const float4 *>(src), n4,
+                                                                       sink, sink_len);
+  return launched();
+}
+
+const char *zero_testkit_last_error(void) { return g_err; }
+
+}  // extern "C"

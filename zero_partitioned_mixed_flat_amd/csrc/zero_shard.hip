@@ -1,0 +1,320 @@
+// zero_shard.hip -- host side of the C ABI declared in include/zero_shard.h:
+// argument validation, the per-step scalars, launch configuration.
+//
+// Sources: "DeepSpeed ZeRO Stages" (sections 2, 2.1, 3.1-3.3), "ZeRO Stage 1
+// Math" ("The core idea", "Where the 12 bytes come from", "The per-step
+// mechanics"), "ZeRO Optimization: Stages 1, 2, and 3 Explained" (Stage 2,
+// mixed precision), "DeepSpeed ZeRO: Extreme Memory Efficiency" (three
+// stages, communication, the optimizer configuration).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "shard_kernels.hpp"
+#include "zero_shard.h"
+
+namespace {
+
+// Launch shape.  Update: U chunks of 4 elements per lane per tile; stats and
+// reduce likewise.  Grids are capped at kBlocksPerCU blocks per CU.
+constexpr int kUpdateU = 4;
+constexpr int kStatsU = 4;
+constexpr int kReduceU = 2;
+constexpr int kReduceG = 8;
+constexpr int kBlocksPerCU = 8;
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ZERO_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Compute units of the current device, cached per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_cache[kMaxDevices];
+
+int cu_count(int *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return ZERO_OK;
+    }
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0)
+    return fail(ZERO_ERR_HIP, "hipDeviceGetAttribute(CU count): %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) g_cu_cache[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return ZERO_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
+
+int grid_for(int64_t len, int64_t tile, int cus, int cap) {
+  const int64_t tiles = ceil_div(len, tile);
+  int64_t g = static_cast<int64_t>(cus) * kBlocksPerCU;
+  if (g > cap) g = cap;
+  if (g > tiles) g = tiles;
+  return static_cast<int>(g < 1 ? 1 : g);
+}
+
+// An error recorded by an earlier, unrelated HIP call on this thread (the
+// runtime keeps the last one) is dropped before a launch, so that the check
+// after it reports only what the launch itself did.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ZERO_OK;
+}
+
+bool scale_valid(double s) { return std::isfinite(s) && s > 0.0; }
+
+// Statistics of `grad` into `stats` through the partials in `ws`.
+int launch_stats(const void *grad, zero_dtype_t dt, int64_t len, float s, zero_grad_stats_t *stats,
+                 void *ws, hipStream_t stream) {
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != ZERO_OK) return st;
+  constexpr int64_t tile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kStatsU;
+  const int grid = grid_for(len, tile, cus, zs::kMaxPartials);
+  zs::Partial *parts = static_cast<zs::Partial *>(ws);
+  clear_stale_error();
+  if (dt == ZERO_F16)
+    zs::grad_stats_kernel<ZERO_F16, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts);
+  else
+    zs::grad_stats_kernel<ZERO_F32, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts);
+  st = check_launch("grad_stats_kernel");
+  if (st != ZERO_OK) return st;
+  zs::finalize_stats_kernel<<<1, zs::kBlock, 0, stream>>>(parts, grid, stats);
+  return check_launch("finalize_stats_kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_partition_layout(int64_t psi, int32_t n_ranks, int32_t rank, int64_t align,
+                          zero_layout_t *out) {
+  if (out == nullptr) return fail(ZERO_ERR_INVALID_ARG, "layout: out is NULL");
+  if (psi < 0) return fail(ZERO_ERR_INVALID_ARG, "layout: psi < 0");
+  if (n_ranks < 1) return fail(ZERO_ERR_INVALID_ARG, "layout: n_ranks < 1");
+  if (rank < 0 || rank >= n_ranks) return fail(ZERO_ERR_INVALID_ARG, "layout: rank out of range");
+  if (align < 1 || (align & (align - 1)) != 0)
+    return fail(ZERO_ERR_INVALID_ARG, "layout: align must be a positive power of two");
+  // the flat space is cut into rows of n_ranks*align elements; each rank
+  // takes `align` elements of every row, as one contiguous block
+  if (align > INT64_MAX / n_ranks) return fail(ZERO_ERR_INT_OVERFLOW, "layout: n_ranks*align overflows");
+  const int64_t row = align * n_ranks;
+  const int64_t rows = ceil_div(psi, row);
+  if (rows > INT64_MAX / row) return fail(ZERO_ERR_INT_OVERFLOW, "layout: padded size overflows");
+  const int64_t shard = rows * align;
+  const int64_t first = shard * rank;
+  out->psi = psi;
+  out->psi_padded = rows * row;
+  out->shard_len = shard;
+  out->offset = first;
+  out->real_len = psi <= first ? 0 : (psi - first < shard ? psi - first : shard);
+  return ok();
+}
+
+int zero_model_state_bytes(double psi, int32_t n_ranks, int32_t stage, double K, double *out_bytes) {
+  if (out_bytes == nullptr) return fail(ZERO_ERR_INVALID_ARG, "model_state_bytes: out is NULL");
+  if (!(psi >= 0.0) || n_ranks < 1 || !(K >= 0.0) || stage < 0 || stage > 3)
+    return fail(ZERO_ERR_INVALID_ARG, "model_state_bytes: bad argument");
+  // bytes per parameter: fp16 compute copy 2, fp16 gradient 2, optimizer K;
+  // each stage divides one more of them by N (P_os, P_os+g, P_os+g+p)
+  const double n = n_ranks;
+  const double param = stage >= 3 ? 2.0 / n : 2.0;
+  const double grad = stage >= 2 ? 2.0 / n : 2.0;
+  const double opt = stage >= 1 ? K / n : K;
+  *out_bytes = (param + grad + opt) * psi;
+  return ok();
+}
+
+size_t zero_workspace_bytes(int64_t len) {
+  if (len < 0) return 0;
+  return static_cast<size_t>(zs::kMaxPartials) * sizeof(zs::Partial);
+}
+
+int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype, int64_t len, double inv_grad_scale,
+                          zero_grad_stats_t *stats, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "grad_stats: len < 0");
+  if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_F32)
+    return fail(ZERO_ERR_INVALID_ARG, "grad_stats: unknown grad dtype");
+  if ((grad == nullptr && len > 0) || stats == nullptr || ws == nullptr)
+    return fail(ZERO_ERR_INVALID_ARG, "grad_stats: NULL pointer");
+  if (!scale_valid(inv_grad_scale))
+    return fail(ZERO_ERR_INVALID_ARG, "grad_stats: inv_grad_scale must be finite and > 0");
+  if (!aligned16(grad) || !aligned16(stats) || !aligned16(ws))
+    return fail(ZERO_ERR_MISALIGNED, "grad_stats: device pointers must be 16-byte aligned");
+  if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "grad_stats: workspace too small");
+  const int st = launch_stats(grad, grad_dtype, len, static_cast<float>(inv_grad_scale), stats, ws, stream);
+  return st == ZERO_OK ? ok() : st;
+}
+
+int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices, int64_t len, float *out_sum,
+                           zero_grad_stats_t *stats, double inv_grad_scale, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (n_slices < 1 || n_slices > ZERO_MAX_SLICES)
+    return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: n_slices must be in [1, %d]", ZERO_MAX_SLICES);
+  if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: len < 0");
+  if (slices == nullptr || (out_sum == nullptr && len > 0))
+    return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: NULL pointer");
+  if (!scale_valid(inv_grad_scale))
+    return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: inv_grad_scale must be finite and > 0");
+  if (len > INT64_MAX / 4) return fail(ZERO_ERR_INT_OVERFLOW, "grad_reduce: len too large");
+  zs::SliceTable tab{};
+  for (int r = 0; r < n_slices; ++r) {
+    if (slices[r] == nullptr && len > 0) return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: slice %d is NULL", r);
+    if (!aligned16(slices[r])) return fail(ZERO_ERR_MISALIGNED, "grad_reduce: slice %d misaligned", r);
+    if (overlap(slices[r], static_cast<size_t>(len) * 2, out_sum, static_cast<size_t>(len) * 4))
+      return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: out_sum overlaps slice %d", r);
+    tab.p[r] = slices[r];
+  }
+  if (!aligned16(out_sum)) return fail(ZERO_ERR_MISALIGNED, "grad_reduce: out_sum misaligned");
+  if (stats != nullptr) {
+    if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: workspace is NULL");
+    if (!aligned16(stats) || !aligned16(ws))
+      return fail(ZERO_ERR_MISALIGNED, "grad_reduce: stats/workspace misaligned");
+    if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "grad_reduce: workspace too small");
+  }
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != ZERO_OK) return st;
+  constexpr int64_t tile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kReduceU;
+  const float s = static_cast<float>(inv_grad_scale);
+  clear_stale_error();
+  if (stats != nullptr) {
+    const int grid = grid_for(len, tile, cus, zs::kMaxPartials);
+    zs::Partial *parts = static_cast<zs::Partial *>(ws);
+    zs::grad_reduce_kernel<true, kReduceU, kReduceG><<<grid, zs::kBlock, 0, stream>>>(tab, n_slices, len, out_sum,
+                                                                                       s, parts);
+    st = check_launch("grad_reduce_kernel");
+    if (st != ZERO_OK) return st;
+    zs::finalize_stats_kernel<<<1, zs::kBlock, 0, stream>>>(parts, grid, stats);
+    st = check_launch("finalize_stats_kernel");
+    if (st != ZERO_OK) return st;
+  } else if (len > 0) {
+    const int grid = grid_for(len, tile, cus, 1 << 30);
+    zs::grad_reduce_kernel<false, kReduceU, kReduceG><<<grid, zs::kBlock, 0, stream>>>(tab, n_slices, len, out_sum,
+                                                                                        s, nullptr);
+    st = check_launch("grad_reduce_kernel");
+    if (st != ZERO_OK) return st;
+  }
+  return ok();
+}
+
+int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+                         float *exp_avg, float *exp_avg_sq, uint16_t *param16, int64_t len, int64_t step,
+                         const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
+                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "adam_step: len < 0");
+  if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_F32)
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: unknown grad dtype");
+  if (hp == nullptr || stats == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: NULL hp or stats");
+  if (len > 0 && (grad == nullptr || master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr ||
+                  param16 == nullptr))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: NULL array");
+  if (step < 1) return fail(ZERO_ERR_INVALID_ARG, "adam_step: step must be >= 1");
+  if (!(std::isfinite(hp->lr) && hp->lr >= 0.0)) return fail(ZERO_ERR_INVALID_ARG, "adam_step: bad lr");
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: betas must be in [0, 1)");
+  if (!(std::isfinite(hp->eps) && hp->eps > 0.0)) return fail(ZERO_ERR_INVALID_ARG, "adam_step: eps must be > 0");
+  if (!scale_valid(inv_grad_scale))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: inv_grad_scale must be finite and > 0");
+  if (len > INT64_MAX / 4) return fail(ZERO_ERR_INT_OVERFLOW, "adam_step: len too large");
+  if (!aligned16(grad) || !aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      !aligned16(param16) || !aligned16(stats))
+    return fail(ZERO_ERR_MISALIGNED, "adam_step: device pointers must be 16-byte aligned");
+  const size_t n = static_cast<size_t>(len);
+  const size_t gbytes = n * (grad_dtype == ZERO_F16 ? 2 : 4);
+  const void *arr[5] = {grad, master, exp_avg, exp_avg_sq, param16};
+  const size_t sz[5] = {gbytes, n * 4, n * 4, n * 4, n * 2};
+  for (int a = 0; a < 5; ++a)
+    for (int b = a + 1; b < 5; ++b)
+      if (overlap(arr[a], sz[a], arr[b], sz[b])) return fail(ZERO_ERR_INVALID_ARG, "adam_step: arrays overlap");
+  if (!stats_precomputed) {
+    if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: workspace is NULL");
+    if (!aligned16(ws)) return fail(ZERO_ERR_MISALIGNED, "adam_step: workspace misaligned");
+    if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "adam_step: workspace too small");
+  }
+
+  // Per-step scalars: each is evaluated in double and rounded once to float.
+  zs::StepScalars c;
+  c.b1 = static_cast<float>(hp->beta1);
+  c.omb1 = static_cast<float>(1.0 - hp->beta1);
+  c.b2 = static_cast<float>(hp->beta2);
+  c.omb2 = static_cast<float>(1.0 - hp->beta2);
+  c.bc1 = static_cast<float>(1.0 - std::pow(hp->beta1, static_cast<double>(step)));
+  c.bc2 = static_cast<float>(1.0 - std::pow(hp->beta2, static_cast<double>(step)));
+  c.lr = static_cast<float>(hp->lr);
+  c.eps = static_cast<float>(hp->eps);
+  c.s = static_cast<float>(inv_grad_scale);
+
+  int st;
+  if (!stats_precomputed) {
+    st = launch_stats(grad, grad_dtype, len, c.s, stats, ws, stream);
+    if (st != ZERO_OK) return st;
+  }
+  if (len == 0) return ok();
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != ZERO_OK) return st;
+  constexpr int64_t tile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kUpdateU;
+  const int grid = grid_for(len, tile, cus, 1 << 30);
+  clear_stale_error();
+  if (grad_dtype == ZERO_F16)
+    zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kBlock, 0, stream>>>(grad, master, exp_avg, exp_avg_sq,
+                                                                                 param16, len, c, stats);
+  else
+    zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kBlock, 0, stream>>>(grad, master, exp_avg, exp_avg_sq,
+                                                                                 param16, len, c, stats);
+  st = check_launch("adam_update_kernel");
+  return st == ZERO_OK ? ok() : st;
+}
+
+const char *zero_status_string(int status) {
+  switch (status) {
+    case ZERO_OK: return "ok";
+    case ZERO_ERR_INVALID_ARG: return "invalid argument";
+    case ZERO_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case ZERO_ERR_WORKSPACE: return "workspace missing or too small";
+    case ZERO_ERR_HIP: return "HIP runtime error";
+    case ZERO_ERR_INT_OVERFLOW: return "size overflows 64 bits";
+    default: return "unknown status";
+  }
+}
+
+const char *zero_last_error(void) { return g_err; }
+
+}  // extern "C"
