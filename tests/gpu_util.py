@@ -76,3 +76,68 @@ def assert_state_parity(gpu, ref, name: str):
         counts[k] = assert_f32_close(a, b, f"{name}.{k}")
     counts["p16"] = assert_f16_close(gpu[3], ref[3], f"{name}.p16")
     return counts
+
+
+# ------------------------------------------------ oracle over large arrays
+# The oracle is single-threaded; at full workload sizes the tests run it on
+# independent contiguous chunks in a thread pool (ctypes releases the GIL).
+# Chunking is exact for the elementwise update and reduce (separability,
+# pinned bit-exact on the CPU); the statistics combine per-chunk flags by OR
+# and per-chunk compensated sums with math.fsum.
+import concurrent.futures as _cf
+import math as _math
+import os as _os
+
+THREADS = max(1, min(16, _os.cpu_count() or 1))
+
+
+def _chunks(n, parts):
+    step = -(-n // parts) if n else 1
+    step = ((step + 1023) // 1024) * 1024
+    return [(a, min(n, a + step)) for a in range(0, n, step)]
+
+
+def oracle_stats_full(g_host, s):
+    import oracle
+    with _cf.ThreadPoolExecutor(THREADS) as ex:
+        res = list(ex.map(lambda ab: oracle.grad_stats(g_host[ab[0]:ab[1]], s), _chunks(g_host.size, 4 * THREADS)))
+    flag = 1 if any(f for f, _ in res) else 0
+    return flag, _math.fsum(x for _, x in res)
+
+
+def oracle_apply_full(g_host, master, m, v, p16, *, step, lr, betas, eps, s, overflow):
+    import oracle
+
+    def run(ab):
+        a, b = ab
+        sl = slice(a, b)
+        return oracle.adam_apply(g_host[sl], master[sl], m[sl], v[sl], p16[sl], step=step, lr=lr,
+                                 beta1=betas[0], beta2=betas[1], eps=eps, inv_scale=s, overflow=overflow)
+    with _cf.ThreadPoolExecutor(THREADS) as ex:
+        assert all(rc == 0 for rc in ex.map(run, _chunks(master.size, 4 * THREADS)))
+
+
+def oracle_reduce_full(slices_host):
+    import numpy as np
+
+    import oracle
+    n = slices_host[0].size
+    out = np.empty(n, dtype=np.float32)
+
+    def run(ab):
+        a, b = ab
+        out[a:b] = oracle.grad_reduce([sl[a:b] for sl in slices_host])
+    with _cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(run, _chunks(n, 4 * THREADS)))
+    return out
+
+
+def stratified_sample(n, count, seed, edge=4096):
+    """One seeded index per stratum of n // count elements, plus the first
+    and last `edge` indices (the ragged tail), sorted and unique."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    stride = n // count
+    idx = np.arange(count, dtype=np.int64) * stride + rng.integers(0, stride, count)
+    idx = np.concatenate([np.arange(min(edge, n)), idx, np.arange(max(0, n - edge), n)])
+    return np.unique(idx[idx < n])

@@ -144,6 +144,23 @@ def test_reduce(dev, n_slices, n):
     assert torch.equal(out, out2)
 
 
+def test_reduce_many_partials(dev):
+    """More than 4096 tiles: the partials are folded in two levels."""
+    import torch
+    n, N = 4096 * 1024 + 777, 3
+    say(f"grad_reduce N={N} n={n} (two-level fold)")
+    slices = [_grad16(n, 99, dev, stream=tk.STREAM_GRAD + r) for r in range(N)]
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stats = zs.new_stats(dev)
+    zs.grad_reduce(slices, out, stats=stats, inv_grad_scale=2.0 ** -18)
+    ref = oracle.grad_reduce([host_u16(t) for t in slices])
+    assert np.array_equal(host_f32(out).view(np.uint32), ref.view(np.uint32))
+    assert_stats(zs.read_stats(stats), oracle.grad_stats(ref, 2.0 ** -18), "reduce two-level fold")
+    slices[2][n - 1] = float("inf")
+    zs.grad_reduce(slices, out, stats=stats, inv_grad_scale=2.0 ** -18)
+    assert zs.read_stats(stats)[0] == 1
+
+
 @pytest.mark.parametrize("special", [np.inf, -np.inf, np.nan])
 def test_reduce_flags_nonfinite_slice(dev, special):
     import torch

@@ -1,0 +1,225 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (statistics call, then the update with the statistics
+precomputed; or the reduce with fused statistics, then the update).  The
+oracle runs on the CPU over the full arrays where that takes seconds, and on
+stratified samples (plus the ragged tail) otherwise; the overflow flag always
+comes from the oracle over the full gradient, except where noted.  Inputs
+follow the workloads' recipes: master ~ N(0,0.02), m ~ N(0,1e-4),
+v ~ |N(0,1e-6)|, fp16 gradients ~ N(0,1e-3) * loss scale (Student-t(3) *
+1e-3 * 2^16 for the unpartitioned run); Adam lr 1e-4, betas (0.9, 0.999),
+eps 1e-8."""
+import numpy as np
+import pytest
+
+import oracle
+import zero_partitioned_mixed_flat_amd as zs
+from zero_partitioned_mixed_flat_amd import testkit as tk
+from gpu_util import (assert_state_parity, assert_stats, host_f32, host_u16, oracle_apply_full,
+                      oracle_reduce_full, oracle_stats_full, require_gpu, say, stratified_sample)
+
+pytestmark = pytest.mark.gpu
+
+LR, BETAS, EPS = 1e-4, (0.9, 0.999), 1e-8
+S16 = 2.0 ** -16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.fixture(autouse=True)
+def _free_cached_memory():
+    import torch
+    yield
+    torch.cuda.empty_cache()
+
+
+def _grad16(n, seed, dev, scale, stream=tk.STREAM_GRAD):
+    import torch
+    return tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), scale, seed, stream)
+
+
+def _bench_step(g, master, m, v, p16, stats, ws, *, step, s):
+    """The benchmark's step: statistics, then the update gated on them."""
+    zs.grad_stats(g, stats, inv_grad_scale=s, workspace=ws)
+    zs.adam_step(g, master, m, v, p16, step=step, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s,
+                 stats=stats, stats_precomputed=True)
+    return zs.read_stats(stats)
+
+
+def _gather(idx_dev, *tensors):
+    out = []
+    for t in tensors:
+        sel = t.index_select(0, idx_dev)
+        out.append(host_u16(sel) if t.element_size() == 2 else host_f32(sel))
+    return out
+
+
+def _apply_sample(g_sample, state, *, step, s, overflow):
+    assert oracle.adam_apply(g_sample, *state, step=step, lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS,
+                             inv_scale=s, overflow=overflow) == 0
+
+
+@pytest.mark.timeout(600)
+def test_gpt2xl_shard_full_arrays(dev):
+    """psi = 1.5e9, N = 4, rank 0 (375,000,064 params), t = 1000; every
+    element compared."""
+    import torch
+    lay = zs.partition_layout(1_500_000_000, 4, 0, 128)
+    n = lay.shard_len
+    say(f"GPT-2-XL shard: n={n}, generating")
+    master, m, v, p16 = tk.init_shard_state(n, 0xC2, zero_moments=False, device=dev)
+    g = _grad16(n, 0xC2, dev, 1e-3 * 65536)
+    torch.cuda.synchronize()
+    g_h = host_u16(g)
+    ref = [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
+    stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+    say("  GPU step")
+    got_stats = _bench_step(g, master, m, v, p16, stats, ws, step=1000, s=S16)
+    say("  oracle statistics and update")
+    ref_stats = oracle_stats_full(g_h, S16)
+    assert_stats(got_stats, ref_stats, "gpt2xl")
+    oracle_apply_full(g_h, *ref, step=1000, lr=LR, betas=BETAS, eps=EPS, s=S16, overflow=ref_stats[0])
+    say("  compare")
+    counts = assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref, "gpt2xl")
+    say("  inexact elements:", counts)
+    assert sum(counts.values()) == 0
+
+
+@pytest.mark.timeout(600)
+def test_7b_n8_shard_sampled_and_inf_run(dev):
+    """psi = 7e9, N = 8, rank 0 (875,000,064 params), t = 1000: a clean run
+    compared on a stratified sample, then a run with 0.001% of the gradient
+    set to +inf whose step must be skipped with every state bit unchanged."""
+    import torch
+    lay = zs.partition_layout(7_000_000_000, 8, 0, 128)
+    n = lay.shard_len
+    say(f"7B/N=8 shard: n={n}, generating")
+    master, m, v, p16 = tk.init_shard_state(n, 0xC4, zero_moments=False, device=dev)
+    g = _grad16(n, 0xC4, dev, 1e-3 * 65536)
+    idx = stratified_sample(n, 2_000_000, 0xC4)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    before = _gather(idx_dev, master, m, v, p16)
+    g_h = host_u16(g)
+    stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+    say("  GPU step (clean)")
+    got = _bench_step(g, master, m, v, p16, stats, ws, step=1000, s=S16)
+    ref_stats = oracle_stats_full(g_h, S16)
+    assert_stats(got, ref_stats, "7b clean")
+    assert ref_stats[0] == 0
+    after = _gather(idx_dev, master, m, v, p16)
+    ref = [a.copy() for a in before]
+    _apply_sample(g_h[idx], ref, step=1000, s=S16, overflow=0)
+    counts = assert_state_parity(after, ref, "7b clean sample")
+    assert sum(counts.values()) == 0
+
+    say("  GPU step (+inf run)")
+    tk.inject_inf_f16_(g, 1e-5, 0xC4F)
+    g_h = host_u16(g)
+    n_inf = int((g_h == 0x7C00).sum())
+    say(f"  injected +inf entries: {n_inf}")
+    assert n_inf > 0
+    snapshot = [t.clone() for t in (master, m, v, p16)]
+    flag, _ = _bench_step(g, master, m, v, p16, stats, ws, step=1001, s=S16)
+    assert flag == oracle_stats_full(g_h, S16)[0] == 1
+    for a, b in zip((master, m, v, p16), snapshot):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.timeout(600)
+def test_7p5b_n64_reduce_then_step(dev):
+    """psi = 7.5e9, N = 64 (117,187,584 params): 64 simulated fp16 slices
+    ~ N(0,1e-3)*2^12 summed on the owner (compared in full), then the step
+    at t = 10 on the fp32 sum with s = 2^-12/64 (compared on a sample)."""
+    import torch
+    lay = zs.partition_layout(7_500_000_000, 64, 0, 128)
+    n = lay.shard_len
+    say(f"7.5B/N=64 shard: n={n}, generating 64 slices")
+    slices = [_grad16(n, 0xC3, dev, 1e-3 * 4096, tk.STREAM_GRAD + r) for r in range(64)]
+    master, m, v, p16 = tk.init_shard_state(n, 0xC3, zero_moments=False, device=dev)
+    s = 2.0 ** -12 / 64
+    gsum = torch.empty(n, dtype=torch.float32, device=dev)
+    stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+    idx = stratified_sample(n, 2_000_000, 0xC3)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    before = _gather(idx_dev, master, m, v, p16)
+    say("  GPU reduce + step")
+    zs.grad_reduce(slices, gsum, stats=stats, inv_grad_scale=s, workspace=ws)
+    red_stats = zs.read_stats(stats)
+    zs.adam_step(gsum, master, m, v, p16, step=10, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s,
+                 stats=stats, stats_precomputed=True)
+    after = _gather(idx_dev, master, m, v, p16)
+    say("  oracle reduce (full)")
+    slices_h = [host_u16(t) for t in slices]
+    del slices
+    ref_sum = oracle_reduce_full(slices_h)
+    del slices_h
+    assert np.array_equal(host_f32(gsum).view(np.uint32), ref_sum.view(np.uint32))
+    ref_stats = oracle_stats_full(ref_sum, s)
+    assert_stats(red_stats, ref_stats, "7.5b reduce")
+    ref = [a.copy() for a in before]
+    _apply_sample(ref_sum[idx], ref, step=10, s=s, overflow=ref_stats[0])
+    counts = assert_state_parity(after, ref, "7.5b step sample")
+    assert sum(counts.values()) == 0
+
+
+@pytest.mark.timeout(900)
+def test_unpartitioned_100_steps_drift(dev):
+    """psi = 1.5e9 at N = 1 (the 16*psi case), 100 Adam steps t = 1..100
+    from m = v = 0 with fresh seeded Student-t(3) * 1e-3 * 2^16 gradients,
+    compared on a 1,048,576-param stratified sample.
+
+    Run 1: gradients redrawn where their fp16 would overflow, so every step
+    applies; the overflow flag and sum of squares are checked against the
+    oracle over the full gradient at steps 1, 25, 50, 75, 100 (in between,
+    the oracle's flag is the sample's, and any disagreement would show in the
+    compared states).  Run 2: 6 steps with the gradients as drawn (about 3.3
+    entries overflow per step, so most steps are skipped); the flag comes
+    from the oracle over the full gradient at every step."""
+    import torch
+    n = 1_500_000_000
+    lay = zs.partition_layout(n, 1, 0, 128)
+    assert lay.shard_len == n and lay.real_len == n
+    say(f"unpartitioned: n={n}, generating state")
+    master, m, v, p16 = tk.init_shard_state(n, 0xC5, zero_moments=True, device=dev)
+    g = torch.empty(n, dtype=torch.float16, device=dev)
+    stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+    idx = stratified_sample(n, 1_048_576, 0xC5, edge=0)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    ref = _gather(idx_dev, master, m, v, p16)
+    t = 0
+    for k in range(100):
+        tk.student_t3_f16_(g, 1e-3 * 65536, 0xC5, tk.STREAM_GRAD + k, redraw_overflow=True)
+        g_s = host_u16(g.index_select(0, idx_dev))
+        flag, ssq = _bench_step(g, master, m, v, p16, stats, ws, step=t + 1, s=S16)
+        if k % 25 == 24 or k == 0:
+            rflag, rssq = oracle_stats_full(host_u16(g), S16)
+            assert_stats((flag, ssq), (rflag, rssq), f"drift step {k + 1}")
+            say(f"  step {k + 1}: full-gradient flag {rflag}, sumsq {rssq:.6e}")
+        else:
+            rflag = oracle.grad_stats(g_s, S16)[0]
+        assert flag == rflag == 0
+        _apply_sample(g_s, ref, step=t + 1, s=S16, overflow=rflag)
+        t += 1
+        if k in (0, 9, 49, 99):
+            counts = assert_state_parity(_gather(idx_dev, master, m, v, p16), ref, f"drift step {k + 1}")
+            say(f"  step {k + 1}: sample inexact {counts}")
+            assert sum(counts.values()) == 0
+
+    applied = 0
+    for k in range(6):
+        tk.student_t3_f16_(g, 1e-3 * 65536, 0xC5, tk.STREAM_GRAD + 1000 + k, redraw_overflow=False)
+        g_full = host_u16(g)
+        rflag, rssq = oracle_stats_full(g_full, S16)
+        flag, ssq = _bench_step(g, master, m, v, p16, stats, ws, step=t + 1, s=S16)
+        assert_stats((flag, ssq), (rflag, rssq), f"literal step {k + 1}")
+        n_inf = int(((g_full & 0x7FFF) == 0x7C00).sum())
+        say(f"  literal step {k + 1}: flag {flag}, fp16 infinities {n_inf}")
+        _apply_sample(g_full[idx], ref, step=t + 1, s=S16, overflow=rflag)
+        if rflag == 0:
+            t += 1
+            applied += 1
+    counts = assert_state_parity(_gather(idx_dev, master, m, v, p16), ref, "literal run")
+    say(f"  literal run: {applied} of 6 steps applied; sample inexact {counts}")
+    assert sum(counts.values()) == 0

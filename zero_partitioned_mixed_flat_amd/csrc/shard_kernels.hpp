@@ -3,15 +3,19 @@
 // ZeRO Stages" section 5.1: the step is O(1) arithmetic per parameter and
 // touches the optimizer state once), so none uses MFMA; the design is about
 // bytes in flight and access shape:
-//   * blocks of 256 threads = four wave64s;
 //   * each lane handles chunks of 4 consecutive elements, so one wave's
 //     access to an fp32 stream is one contiguous 1 KiB (16 B per lane) and to
 //     an fp16 stream one contiguous 512 B (8 B per lane);
 //   * U chunks per lane are loaded before any is used, to keep enough loads
 //     outstanding per CU to cover HBM latency;
-//   * grid-stride loops over tiles, with the grid sized from the CU count;
+//   * the update runs one tile per block over a grid of all tiles, with
+//     non-temporal loads and stores (the state streams are touched once per
+//     step and are far larger than the caches); measured on MI355X this beats
+//     grid-stride persistent blocks by 8-10%;
+//   * the statistics and the reduce use grid-stride loops over a grid sized
+//     from the CU count, since each block leaves one partial result;
 //   * reductions of the statistics: per-lane fp64 accumulation, butterfly
-//     shuffles inside the wave, LDS across the four waves, one partial per
+//     shuffles inside the wave, LDS across the block's waves, one partial per
 //     block, then a single-block pass over the partials in index order.
 #pragma once
 
@@ -22,10 +26,25 @@
 
 namespace zs {
 
-constexpr int kBlock = 256;  // threads per block
-constexpr int kWave = 64;    // CDNA wavefront width
-constexpr int kChunk = 4;    // consecutive elements per lane per access
-constexpr int kMaxPartials = 2048;
+constexpr int kBlock = 256;        // threads per block (statistics, reduce)
+constexpr int kUpdateBlock = 128;  // threads per block (update)
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kChunk = 4;          // consecutive elements per lane per access
+constexpr int kMaxPartials = 2048; // partials of the grid-stride statistics kernel
+constexpr int kFold = kBlock * 16;  // partials folded by one block of the first fold level
+
+// Native vector types for the non-temporal load/store builtins.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ T stream_load(const T *p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void stream_store(T *p, T v) {
+  __builtin_nontemporal_store(v, p);
+}
 
 // Per-step constants, each derived in double on the host and rounded once.
 struct StepScalars {
@@ -208,46 +227,65 @@ __global__ __launch_bounds__(kBlock) void finalize_stats_kernel(const Partial *_
   }
 }
 
+// First level of folding many partials: block b folds the contiguous range
+// [b*kFold, (b+1)*kFold) in a fixed order into out[b].
+__global__ __launch_bounds__(kBlock) void fold_partials_kernel(const Partial *__restrict__ in, int64_t n,
+                                                               Partial *__restrict__ out) {
+  const int64_t begin = static_cast<int64_t>(blockIdx.x) * kFold;
+  double ssq = 0.0;
+  uint32_t flag = 0u;
+#pragma unroll
+  for (int i = 0; i < kFold / kBlock; ++i) {
+    const int64_t j = begin + i * kBlock + threadIdx.x;
+    if (j < n) {
+      ssq += in[j].sumsq;
+      flag |= in[j].flag;
+    }
+  }
+  block_partial(ssq, flag, &out[blockIdx.x]);
+}
+
 // -------------------------------------------------------------------- reduce
 // Owner-side reduce of N fp16 slices into fp32, left fold in rank order,
-// optionally with the statistics of (sum * s) in the same pass.  Slices are
-// read G at a time so G*U loads are in flight before the in-order adds.
+// optionally with the statistics of (sum * s) in the same pass.  One block
+// per tile of kBlock*4*U elements (one partial per block); slices are read G
+// at a time with non-temporal loads so G*U loads are in flight before the
+// in-order adds.
 template <bool WITH_STATS, int U, int G>
 __global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int n, int64_t len,
                                                              float *__restrict__ out, float s,
                                                              Partial *__restrict__ partials) {
 #pragma clang fp contract(off)
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kChunk * U;
+  constexpr int kSpan = kBlock * kChunk;
+  constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
   double acc0 = 0.0, acc1 = 0.0;
   uint32_t flag = 0u;
+  // addresses = a tile base that is the same for the whole block (kept in
+  // scalar registers) + a 32-bit lane offset; with per-lane 64-bit addresses
+  // the compiler serialises the slice loads
+  const uint32_t lane = threadIdx.x * kChunk;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t base = tile * kTile;
-    if (base + kTile <= len) {
+    const int64_t tbase = tile * kTile;
+    if (tbase + kTile <= len) {
       float acc[U][kChunk];
-      {
-        uint2 raw[U];
 #pragma unroll
-        for (int k = 0; k < U; ++k)
-          raw[k] = *reinterpret_cast<const uint2 *>(tab.p[0] + base + k * (kBlock * kChunk) + threadIdx.x * kChunk);
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-          acc[k][0] = h2f(raw[k].x & 0xFFFFu);
-          acc[k][1] = h2f(raw[k].x >> 16);
-          acc[k][2] = h2f(raw[k].y & 0xFFFFu);
-          acc[k][3] = h2f(raw[k].y >> 16);
-        }
+      for (int k = 0; k < U; ++k) {
+        const u32x2 raw = stream_load(reinterpret_cast<const u32x2 *>(tab.p[0] + tbase + lane + k * kSpan));
+        acc[k][0] = h2f(raw.x & 0xFFFFu);
+        acc[k][1] = h2f(raw.x >> 16);
+        acc[k][2] = h2f(raw.y & 0xFFFFu);
+        acc[k][3] = h2f(raw.y >> 16);
       }
       for (int r0 = 1; r0 < n; r0 += G) {
         const int cnt = (n - r0) < G ? (n - r0) : G;
-        uint2 raw[G][U];
+        u32x2 raw[G][U];
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           if (q < cnt) {
-            const uint16_t *p = tab.p[r0 + q];
+            const uint16_t *p = tab.p[r0 + q] + tbase;
 #pragma unroll
-            for (int k = 0; k < U; ++k)
-              raw[q][k] = *reinterpret_cast<const uint2 *>(p + base + k * (kBlock * kChunk) + threadIdx.x * kChunk);
+            for (int k = 0; k < U; ++k) raw[q][k] = stream_load(reinterpret_cast<const u32x2 *>(p + lane + k * kSpan));
           }
         }
 #pragma unroll
@@ -265,8 +303,8 @@ __global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk;
-        *reinterpret_cast<float4 *>(out + j) = make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
+        stream_store(reinterpret_cast<f32x4 *>(out + tbase + lane + k * kSpan),
+                     f32x4{acc[k][0], acc[k][1], acc[k][2], acc[k][3]});
         if constexpr (WITH_STATS) {
 #pragma unroll
           for (int e = 0; e < kChunk; ++e) {
@@ -283,7 +321,7 @@ __global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int
       for (int k = 0; k < U; ++k) {
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
-          const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk + e;
+          const int64_t j = tbase + lane + k * kSpan + e;
           if (j < len) {
             float a = h2f(tab.p[0][j]);
             for (int r = 1; r < n; ++r) a = a + h2f(tab.p[r][j]);
@@ -304,59 +342,66 @@ __global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int
 // Fused single pass over the shard: read g, m, v, master; write m, v, master
 // and the fp16 copy (28 B per parameter with an fp16 gradient, 30 B with
 // fp32).  Every block first reads the device-resident overflow flag and
-// leaves before any memory access to the states if it is set.
+// leaves before any memory access to the states if it is set.  Launched with
+// one block per tile of kUpdateBlock*4*U elements.
 template <zero_dtype_t DT, int U>
-__global__ __launch_bounds__(kBlock) void adam_update_kernel(
+__global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     const void *__restrict__ grad, float *__restrict__ master, float *__restrict__ m,
     float *__restrict__ v, uint16_t *__restrict__ p16, int64_t len, StepScalars c,
     const zero_grad_stats_t *__restrict__ stats) {
   if (stats->overflow != 0u) return;
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kChunk * U;
+  constexpr int kSpan = kUpdateBlock * kChunk;  // elements of one chunk row of the block
+  constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
+  const uint32_t lane = threadIdx.x * kChunk;  // see the note in the reduce kernel
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t base = tile * kTile;
-    if (base + kTile <= len) {
+    const int64_t tbase = tile * kTile;
+    if (tbase + kTile <= len) {
+      const float *tm = m + tbase, *tv = v + tbase, *tt0 = master + tbase;
       float x[U][kChunk];
-      float4 mm[U], vv[U], tt[U];
+      f32x4 mm[U], vv[U], tt[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk;
+        const uint32_t j = lane + k * kSpan;
         if constexpr (DT == ZERO_F16) {
-          const uint2 raw = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(grad) + j);
+          const u32x2 raw =
+              stream_load(reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(grad) + tbase + j));
           x[k][0] = h2f(raw.x & 0xFFFFu);
           x[k][1] = h2f(raw.x >> 16);
           x[k][2] = h2f(raw.y & 0xFFFFu);
           x[k][3] = h2f(raw.y >> 16);
         } else {
-          const float4 raw = *reinterpret_cast<const float4 *>(static_cast<const float *>(grad) + j);
+          const f32x4 raw = stream_load(reinterpret_cast<const f32x4 *>(static_cast<const float *>(grad) + tbase + j));
           x[k][0] = raw.x;
           x[k][1] = raw.y;
           x[k][2] = raw.z;
           x[k][3] = raw.w;
         }
-        mm[k] = *reinterpret_cast<const float4 *>(m + j);
-        vv[k] = *reinterpret_cast<const float4 *>(v + j);
-        tt[k] = *reinterpret_cast<const float4 *>(master + j);
+        mm[k] = stream_load(reinterpret_cast<const f32x4 *>(tm + j));
+        vv[k] = stream_load(reinterpret_cast<const f32x4 *>(tv + j));
+        tt[k] = stream_load(reinterpret_cast<const f32x4 *>(tt0 + j));
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        uint32_t h0, h1, h2, h3;
-        adam_element(x[k][0], mm[k].x, vv[k].x, tt[k].x, h0, c);
-        adam_element(x[k][1], mm[k].y, vv[k].y, tt[k].y, h1, c);
-        adam_element(x[k][2], mm[k].z, vv[k].z, tt[k].z, h2, c);
-        adam_element(x[k][3], mm[k].w, vv[k].w, tt[k].w, h3, c);
-        const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk;
-        *reinterpret_cast<float4 *>(m + j) = mm[k];
-        *reinterpret_cast<float4 *>(v + j) = vv[k];
-        *reinterpret_cast<float4 *>(master + j) = tt[k];
-        *reinterpret_cast<uint2 *>(p16 + j) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        float ma[kChunk] = {mm[k].x, mm[k].y, mm[k].z, mm[k].w};
+        float va[kChunk] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+        float ta[kChunk] = {tt[k].x, tt[k].y, tt[k].z, tt[k].w};
+        uint32_t h[kChunk];
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) adam_element(x[k][e], ma[e], va[e], ta[e], h[e], c);
+        const uint32_t j = lane + k * kSpan;
+        stream_store(reinterpret_cast<f32x4 *>(m + tbase + j), f32x4{ma[0], ma[1], ma[2], ma[3]});
+        stream_store(reinterpret_cast<f32x4 *>(v + tbase + j), f32x4{va[0], va[1], va[2], va[3]});
+        stream_store(reinterpret_cast<f32x4 *>(master + tbase + j), f32x4{ta[0], ta[1], ta[2], ta[3]});
+        stream_store(reinterpret_cast<u32x2 *>(p16 + tbase + j), u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
       }
     } else {
+      // the ragged last tile, element by element
 #pragma unroll
       for (int k = 0; k < U; ++k) {
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
-          const int64_t j = base + k * (kBlock * kChunk) + threadIdx.x * kChunk + e;
+          const int64_t j = tbase + lane + k * kSpan + e;
           if (j < len) {
             float x;
             if constexpr (DT == ZERO_F16)

@@ -20,12 +20,14 @@
 
 namespace {
 
-// Launch shape.  Update: U chunks of 4 elements per lane per tile; stats and
-// reduce likewise.  Grids are capped at kBlocksPerCU blocks per CU.
-constexpr int kUpdateU = 4;
+// Launch shape.  Update: U chunks of 4 elements per lane per tile, one block
+// per tile.  Stats and reduce: U chunks per lane per tile, grids capped at
+// kBlocksPerCU blocks per CU.
+constexpr int kUpdateU = 2;
 constexpr int kStatsU = 4;
-constexpr int kReduceU = 2;
-constexpr int kReduceG = 8;
+constexpr int kReduceU = 1;
+constexpr int kReduceG = 16;
+constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kReduceU;
 constexpr int kBlocksPerCU = 8;
 
 thread_local char g_err[512] = "";
@@ -99,6 +101,30 @@ int check_launch(const char *what) {
 
 bool scale_valid(double s) { return std::isfinite(s) && s > 0.0; }
 
+// Partials of the reduce: one per tile (at least one, for len = 0), then the
+// first-level folds of kFold partials each.
+int64_t reduce_partials(int64_t len) {
+  const int64_t t = ceil_div(len, kReduceTile);
+  return t < 1 ? 1 : t;
+}
+int64_t fold_blocks(int64_t nparts) { return ceil_div(nparts, zs::kFold); }
+
+// Folds `nparts` per-block partials in `ws` into `stats`, in a fixed order:
+// directly when they fit one block's pass, else through one fold level.
+int finalize(zs::Partial *parts, int64_t nparts, zero_grad_stats_t *stats, hipStream_t stream) {
+  if (nparts <= zs::kFold) {
+    zs::finalize_stats_kernel<<<1, zs::kBlock, 0, stream>>>(parts, static_cast<int>(nparts), stats);
+    return check_launch("finalize_stats_kernel");
+  }
+  const int64_t nfold = fold_blocks(nparts);
+  zs::Partial *folded = parts + nparts;
+  zs::fold_partials_kernel<<<static_cast<unsigned>(nfold), zs::kBlock, 0, stream>>>(parts, nparts, folded);
+  const int st = check_launch("fold_partials_kernel");
+  if (st != ZERO_OK) return st;
+  zs::finalize_stats_kernel<<<1, zs::kBlock, 0, stream>>>(folded, static_cast<int>(nfold), stats);
+  return check_launch("finalize_stats_kernel");
+}
+
 // Statistics of `grad` into `stats` through the partials in `ws`.
 int launch_stats(const void *grad, zero_dtype_t dt, int64_t len, float s, zero_grad_stats_t *stats,
                  void *ws, hipStream_t stream) {
@@ -115,8 +141,7 @@ int launch_stats(const void *grad, zero_dtype_t dt, int64_t len, float s, zero_g
     zs::grad_stats_kernel<ZERO_F32, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts);
   st = check_launch("grad_stats_kernel");
   if (st != ZERO_OK) return st;
-  zs::finalize_stats_kernel<<<1, zs::kBlock, 0, stream>>>(parts, grid, stats);
-  return check_launch("finalize_stats_kernel");
+  return finalize(parts, grid, stats, stream);
 }
 
 }  // namespace
@@ -163,7 +188,11 @@ int zero_model_state_bytes(double psi, int32_t n_ranks, int32_t stage, double K,
 
 size_t zero_workspace_bytes(int64_t len) {
   if (len < 0) return 0;
-  return static_cast<size_t>(zs::kMaxPartials) * sizeof(zs::Partial);
+  // the larger of the statistics kernel's partials and the reduce's (one per
+  // tile of kReduceTile elements plus their first fold level)
+  const int64_t red = reduce_partials(len) + fold_blocks(reduce_partials(len));
+  const int64_t n = red > zs::kMaxPartials ? red : zs::kMaxPartials;
+  return static_cast<size_t>(n) * sizeof(zs::Partial);
 }
 
 int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype, int64_t len, double inv_grad_scale,
@@ -208,24 +237,22 @@ int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices, int6
       return fail(ZERO_ERR_MISALIGNED, "grad_reduce: stats/workspace misaligned");
     if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "grad_reduce: workspace too small");
   }
-  int cus = 0;
-  int st = cu_count(&cus);
-  if (st != ZERO_OK) return st;
-  constexpr int64_t tile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kReduceU;
+  // one block per tile: every block writes its own partial
+  const int64_t nparts = reduce_partials(len);
+  if (nparts > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "grad_reduce: len too large");
+  const unsigned grid = static_cast<unsigned>(nparts);
   const float s = static_cast<float>(inv_grad_scale);
+  int st;
   clear_stale_error();
   if (stats != nullptr) {
-    const int grid = grid_for(len, tile, cus, zs::kMaxPartials);
     zs::Partial *parts = static_cast<zs::Partial *>(ws);
     zs::grad_reduce_kernel<true, kReduceU, kReduceG><<<grid, zs::kBlock, 0, stream>>>(tab, n_slices, len, out_sum,
                                                                                        s, parts);
     st = check_launch("grad_reduce_kernel");
     if (st != ZERO_OK) return st;
-    zs::finalize_stats_kernel<<<1, zs::kBlock, 0, stream>>>(parts, grid, stats);
-    st = check_launch("finalize_stats_kernel");
+    st = finalize(parts, nparts, stats, stream);
     if (st != ZERO_OK) return st;
   } else if (len > 0) {
-    const int grid = grid_for(len, tile, cus, 1 << 30);
     zs::grad_reduce_kernel<false, kReduceU, kReduceG><<<grid, zs::kBlock, 0, stream>>>(tab, n_slices, len, out_sum,
                                                                                         s, nullptr);
     st = check_launch("grad_reduce_kernel");
@@ -287,18 +314,16 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
     if (st != ZERO_OK) return st;
   }
   if (len == 0) return ok();
-  int cus = 0;
-  st = cu_count(&cus);
-  if (st != ZERO_OK) return st;
-  constexpr int64_t tile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kUpdateU;
-  const int grid = grid_for(len, tile, cus, 1 << 30);
+  constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * kUpdateU;
+  const int64_t tiles = ceil_div(len, tile);
+  const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
   clear_stale_error();
   if (grad_dtype == ZERO_F16)
-    zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kBlock, 0, stream>>>(grad, master, exp_avg, exp_avg_sq,
-                                                                                 param16, len, c, stats);
+    zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kUpdateBlock, 0, stream>>>(
+        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
   else
-    zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kBlock, 0, stream>>>(grad, master, exp_avg, exp_avg_sq,
-                                                                                 param16, len, c, stats);
+    zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kUpdateBlock, 0, stream>>>(
+        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
   st = check_launch("adam_update_kernel");
   return st == ZERO_OK ? ok() : st;
 }
