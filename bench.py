@@ -39,6 +39,7 @@ UPDATE_BYTES_PER_PARAM = 28      # read g2 m4 v4 th4, write m4 v4 th4 p16 2
 STATS_BYTES_PER_PARAM = 2        # read g2
 REDUCE_BYTES_PER_PARAM = lambda n: 2 * n + 4   # noqa: E731
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_update_gpt2xl_shard_counters.txt")
+REDUCE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "grad_reduce_7p5b_n64_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc", f)
                   for f in ("shard_kernels.hpp", "zero_shard.hip")]
 
@@ -59,13 +60,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per update launch from the committed rocprofv3 counter
-    summary, or None when it is missing or was taken for other kernel code."""
-    if not os.path.exists(COUNTERS_FILE):
+def counter_traffic(path=COUNTERS_FILE):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when it is missing or was taken for other kernel code."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -124,7 +125,8 @@ def reduce_secondary(torch, zs, tk, dev, steps):
     return {"workload": "7.5B model at N=64: owner-side sum of 64 fp16 slices of a 117,187,584-param shard "
                         "into fp32 with fused flag/sum of squares",
             "ms": round(sec * 1e3, 4), "params_per_s": n / sec, "hbm_gbps": round(gbps, 1),
-            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": REDUCE_BYTES_PER_PARAM(64)}
+            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": REDUCE_BYTES_PER_PARAM(64),
+            "traffic": counter_traffic(REDUCE_COUNTERS_FILE)}
 
 
 def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
@@ -170,9 +172,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one rank's shard step on one GPU; runs on more than one GPU are not "
-              "part of this build (each rank's step is independent, so per-rank throughput is the "
-              "one-GPU figure).", file=sys.stderr)
+        print("bench.py measures one rank's shard step on one GPU and supports --gpus 1 only: each "
+              "rank's step is independent of the others, so the per-rank throughput is the one-GPU "
+              "figure; the multi-GPU exchange is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -58,8 +58,9 @@ int zero_testkit_inject_inf_f16(uint16_t *out, int64_t n, double prob, uint64_t 
 
 /* Plain streaming kernels that set the attainable HBM ceiling and calibrate
  * the FETCH_SIZE / WRITE_SIZE counters: dst = src over n floats (8 B of
- * traffic per element); and a read of n floats whose per-block sums go to
- * sink[block] (4 B per element). */
+ * traffic per element; 16-byte aligned pointers); and a read of the first
+ * floor(n/4)*4 floats whose per-block sums go to sink[block] for the blocks
+ * below sink_len (4 B per element; at most 4 blocks per CU are launched). */
 int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream_);
 int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len,
                           hipStream_t stream_);
