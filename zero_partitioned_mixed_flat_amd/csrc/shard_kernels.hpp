@@ -8,10 +8,15 @@
 //     an fp16 stream one contiguous 512 B (8 B per lane);
 //   * U chunks per lane are loaded before any is used, to keep enough loads
 //     outstanding per CU to cover HBM latency;
-//   * the update runs one tile per block over a grid of all tiles, with
-//     non-temporal loads and stores (the state streams are touched once per
-//     step and are far larger than the caches); measured on MI355X this beats
-//     grid-stride persistent blocks by 8-10%;
+//   * the update and the reduce run one tile per block over a grid of all
+//     tiles, with non-temporal loads and stores (the streams are touched
+//     once per step and are far larger than the caches); measured on MI355X
+//     this beats grid-stride persistent blocks by 8-10%;
+//   * their resident blocks per CU are capped (the host launches them with
+//     an otherwise unused dynamic LDS allocation sized for the cap): with 4
+//     to 64 concurrent streams, fewer requests in flight per CU let the
+//     memory controllers keep DRAM rows open, which measured 6-8% faster
+//     than full occupancy;
 //   * the statistics and the reduce use grid-stride loops over a grid sized
 //     from the CU count, since each block leaves one partial result;
 //   * reductions of the statistics: per-lane fp64 accumulation, butterfly
@@ -26,8 +31,9 @@
 
 namespace zs {
 
-constexpr int kBlock = 256;        // threads per block (statistics, reduce)
-constexpr int kUpdateBlock = 128;  // threads per block (update)
+constexpr int kBlock = 256;        // threads per block (statistics, folds)
+constexpr int kReduceBlock = 128;  // threads per block (reduce)
+constexpr int kUpdateBlock = 64;   // threads per block (update): one wave
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kChunk = 4;          // consecutive elements per lane per access
 constexpr int kMaxPartials = 2048; // partials of the grid-stride statistics kernel
@@ -100,15 +106,18 @@ __device__ __forceinline__ void adam_element(float x, float &m, float &v, float 
   p16 = f2h(th1);
 }
 
-// Sum of a double and OR of a flag over the block; thread 0 stores them.
+// Sum of a double and OR of a flag over a block of BS threads; thread 0
+// stores them.
+template <int BS = kBlock>
 __device__ __forceinline__ void block_partial(double ssq, uint32_t flag, Partial *out) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     ssq += __shfl_xor(ssq, off, kWave);
     flag |= __shfl_xor(flag, off, kWave);
   }
-  __shared__ double s_ssq[kBlock / kWave];
-  __shared__ uint32_t s_flag[kBlock / kWave];
+  static_assert(BS % kWave == 0, "whole waves");
+  __shared__ double s_ssq[BS / kWave];
+  __shared__ uint32_t s_flag[BS / kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   if (lane == 0) {
@@ -120,7 +129,7 @@ __device__ __forceinline__ void block_partial(double ssq, uint32_t flag, Partial
     double t = s_ssq[0];
     uint32_t f = s_flag[0];
 #pragma unroll
-    for (int w = 1; w < kBlock / kWave; ++w) {
+    for (int w = 1; w < BS / kWave; ++w) {
       t += s_ssq[w];
       f |= s_flag[w];
     }
@@ -248,15 +257,15 @@ __global__ __launch_bounds__(kBlock) void fold_partials_kernel(const Partial *__
 // -------------------------------------------------------------------- reduce
 // Owner-side reduce of N fp16 slices into fp32, left fold in rank order,
 // optionally with the statistics of (sum * s) in the same pass.  One block
-// per tile of kBlock*4*U elements (one partial per block); slices are read G
-// at a time with non-temporal loads so G*U loads are in flight before the
-// in-order adds.
+// per tile of kReduceBlock*4*U elements (one partial per block); slices are
+// read G at a time with non-temporal loads so G*U loads are in flight before
+// the in-order adds.
 template <bool WITH_STATS, int U, int G>
-__global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int n, int64_t len,
-                                                             float *__restrict__ out, float s,
-                                                             Partial *__restrict__ partials) {
+__global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable tab, int n, int64_t len,
+                                                                   float *__restrict__ out, float s,
+                                                                   Partial *__restrict__ partials) {
 #pragma clang fp contract(off)
-  constexpr int kSpan = kBlock * kChunk;
+  constexpr int kSpan = kReduceBlock * kChunk;
   constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
   double acc0 = 0.0, acc1 = 0.0;
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int
       }
     }
   }
-  if constexpr (WITH_STATS) block_partial(acc0 + acc1, flag, &partials[blockIdx.x]);
+  if constexpr (WITH_STATS) block_partial<kReduceBlock>(acc0 + acc1, flag, &partials[blockIdx.x]);
 }
 
 // ---------------------------------------------------------------- the update
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(kBlock) void grad_reduce_kernel(SliceTable tab, int
 // and the fp16 copy (28 B per parameter with an fp16 gradient, 30 B with
 // fp32).  Every block first reads the device-resident overflow flag and
 // leaves before any memory access to the states if it is set.  Launched with
-// one block per tile of kUpdateBlock*4*U elements.
+// one block (one wave) per tile of kUpdateBlock*4*U elements.
 template <zero_dtype_t DT, int U>
 __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     const void *__restrict__ grad, float *__restrict__ master, float *__restrict__ m,

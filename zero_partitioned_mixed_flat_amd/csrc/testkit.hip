@@ -120,7 +120,7 @@ __global__ void inject_inf_kernel(uint16_t *out, int64_t n, double prob, uint64_
 
 // Reference streaming kernels in the shapes that measured fastest on MI355X:
 // copy = one 16-byte non-temporal load and store per lane, 64-lane blocks,
-// one block per 1024 floats; read = four 16-byte non-temporal loads per lane
+// one block per 256 floats; read = four 16-byte non-temporal loads per lane
 // per iteration over a grid of four blocks per CU.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCopyBlock = 64;

@@ -27,8 +27,11 @@ constexpr int kUpdateU = 2;
 constexpr int kStatsU = 4;
 constexpr int kReduceU = 1;
 constexpr int kReduceG = 16;
-constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kReduceU;
+constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
 constexpr int kBlocksPerCU = 8;
+// Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
+constexpr int kUpdateBlocksPerCU = 8;
+constexpr int kReduceBlocksPerCU = 6;
 
 thread_local char g_err[512] = "";
 
@@ -79,6 +82,58 @@ int cu_count(int *out) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
+
+// Dynamic LDS bytes per block that leave room for exactly `target` resident
+// blocks of `kernel` on a CU (0 when the kernel's own resources already allow
+// no more than that, or when no size gives exactly `target`).  Found once per
+// device and kernel with the occupancy API and cached.
+enum CapKernel { kCapUpdateF16, kCapUpdateF32, kCapReduceStats, kCapReduce, kCapKinds };
+std::atomic<int> g_lds_cache[kMaxDevices][kCapKinds];
+std::atomic<bool> g_lds_init{false};
+
+template <typename K>
+int occupancy_cap_lds(CapKernel which, K kernel, int block, int target, size_t *lds_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (!g_lds_init.load(std::memory_order_acquire)) {
+    for (auto &row : g_lds_cache)
+      for (auto &x : row) x.store(-1, std::memory_order_relaxed);
+    g_lds_init.store(true, std::memory_order_release);
+  }
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_lds_cache[dev][which].load(std::memory_order_relaxed);
+    if (cached >= 0) {
+      *lds_out = static_cast<size_t>(cached);
+      return ZERO_OK;
+    }
+  }
+  int lds_cu = 0, lds_block = 0, occ = 0;
+  e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0);
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  int chosen = 0;
+  if (occ > target && lds_cu > 0) {
+    // start at an even share of the CU's LDS and step down until exactly
+    // `target` blocks fit
+    int lds = (lds_cu / target) & ~127;
+    if (lds > lds_block) lds = lds_block & ~127;
+    for (int i = 0; i < 64 && lds >= 128; ++i, lds -= 128) {
+      int o = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, block, static_cast<size_t>(lds));
+      if (e != hipSuccess) return fail(ZERO_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+      if (o == target) {
+        chosen = lds;
+        break;
+      }
+      if (o > target) break;
+    }
+  }
+  if (dev >= 0 && dev < kMaxDevices) g_lds_cache[dev][which].store(chosen, std::memory_order_relaxed);
+  *lds_out = static_cast<size_t>(chosen);
+  return ZERO_OK;
+}
 
 int grid_for(int64_t len, int64_t tile, int cus, int cap) {
   const int64_t tiles = ceil_div(len, tile);
@@ -243,18 +298,26 @@ int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices, int6
   const unsigned grid = static_cast<unsigned>(nparts);
   const float s = static_cast<float>(inv_grad_scale);
   int st;
-  clear_stale_error();
+  size_t lds = 0;
   if (stats != nullptr) {
+    st = occupancy_cap_lds(kCapReduceStats, zs::grad_reduce_kernel<true, kReduceU, kReduceG>, zs::kReduceBlock,
+                           kReduceBlocksPerCU, &lds);
+    if (st != ZERO_OK) return st;
     zs::Partial *parts = static_cast<zs::Partial *>(ws);
-    zs::grad_reduce_kernel<true, kReduceU, kReduceG><<<grid, zs::kBlock, 0, stream>>>(tab, n_slices, len, out_sum,
-                                                                                       s, parts);
+    clear_stale_error();
+    zs::grad_reduce_kernel<true, kReduceU, kReduceG><<<grid, zs::kReduceBlock, lds, stream>>>(
+        tab, n_slices, len, out_sum, s, parts);
     st = check_launch("grad_reduce_kernel");
     if (st != ZERO_OK) return st;
     st = finalize(parts, nparts, stats, stream);
     if (st != ZERO_OK) return st;
   } else if (len > 0) {
-    zs::grad_reduce_kernel<false, kReduceU, kReduceG><<<grid, zs::kBlock, 0, stream>>>(tab, n_slices, len, out_sum,
-                                                                                        s, nullptr);
+    st = occupancy_cap_lds(kCapReduce, zs::grad_reduce_kernel<false, kReduceU, kReduceG>, zs::kReduceBlock,
+                           kReduceBlocksPerCU, &lds);
+    if (st != ZERO_OK) return st;
+    clear_stale_error();
+    zs::grad_reduce_kernel<false, kReduceU, kReduceG><<<grid, zs::kReduceBlock, lds, stream>>>(
+        tab, n_slices, len, out_sum, s, nullptr);
     st = check_launch("grad_reduce_kernel");
     if (st != ZERO_OK) return st;
   }
@@ -317,12 +380,20 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
   constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * kUpdateU;
   const int64_t tiles = ceil_div(len, tile);
   const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
+  size_t lds = 0;
+  if (grad_dtype == ZERO_F16)
+    st = occupancy_cap_lds(kCapUpdateF16, zs::adam_update_kernel<ZERO_F16, kUpdateU>, zs::kUpdateBlock,
+                           kUpdateBlocksPerCU, &lds);
+  else
+    st = occupancy_cap_lds(kCapUpdateF32, zs::adam_update_kernel<ZERO_F32, kUpdateU>, zs::kUpdateBlock,
+                           kUpdateBlocksPerCU, &lds);
+  if (st != ZERO_OK) return st;
   clear_stale_error();
   if (grad_dtype == ZERO_F16)
-    zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kUpdateBlock, 0, stream>>>(
+    zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kUpdateBlock, lds, stream>>>(
         grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
   else
-    zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kUpdateBlock, 0, stream>>>(
+    zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kUpdateBlock, lds, stream>>>(
         grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
   st = check_launch("adam_update_kernel");
   return st == ZERO_OK ? ok() : st;
