@@ -237,9 +237,25 @@ def main():
 
     secondary = None
     if not args.no_secondary:
+        # the same update with global-norm clipping active (max norm 1; this
+        # gradient's norm is about 19): the factor comes from the device sum
+        # of squares, so the kernel's traffic is unchanged
+        zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
+        clip_ms = []
+        for k in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            zs.adam_step(g, master, m, v, p16, step=T0 + 100 + k, lr=LR, betas=BETAS, eps=EPS,
+                         inv_grad_scale=INV_SCALE, max_grad_norm=1.0, stats=stats, stats_precomputed=True)
+            b.record()
+            clip_ms.append((a, b))
+        torch.cuda.synchronize()
+        clip_avg = sum(a.elapsed_time(b) for a, b in clip_ms) / len(clip_ms)
         del ws
-        secondary = reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2))
-        log(f"reduce N=64: {secondary}")
+        secondary = {"clipped_update": {"max_grad_norm": 1.0, "avg_launch_ms": round(clip_avg, 4),
+                                        "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},
+                     "reduce_n64": reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
+        log(f"secondary: {secondary}")
 
     cpu = None
     if not args.no_cpu_baseline:

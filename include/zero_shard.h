@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 1
+#define ZERO_SHARD_ABI_VERSION 2
 /* Largest number of simulated rank slices one reduce call accepts. */
 #define ZERO_MAX_SLICES 64
 
@@ -65,12 +65,20 @@ typedef struct {
 } zero_layout_t;
 
 /* Adam hyperparameters, named as in the optimizer block of the DeepSpeed
- * configuration shown on [DZE] (lr, betas, eps).  No weight decay. */
+ * configuration shown on [DZE] (lr, betas, eps).  No weight decay.
+ * max_grad_norm: global-norm gradient clipping ([ZS] section 2.1: clipping
+ * needs ||g||_2 over all of P, one scalar all-reduce).  When > 0 and the
+ * norm sqrt(stats->sumsq) of the unscaled gradient exceeds it, the gradient
+ * is multiplied by max_grad_norm / norm; the factor is folded into the
+ * unscale multiplier, (float)(inv_grad_scale * factor) computed in double and
+ * rounded once.  0 disables clipping (the multiplier is then exactly
+ * (float)inv_grad_scale). */
 typedef struct {
   double lr;
   double beta1;
   double beta2;
   double eps;
+  double max_grad_norm;
 } zero_adam_hparams_t;
 
 /* Device-resident result of the gradient statistics. */
@@ -189,9 +197,13 @@ int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype,
  * Overflow: when stats->overflow is 1 every block exits before touching the
  * states; master, exp_avg, exp_avg_sq and param16 keep their bits and the
  * caller should not advance t (the decision never needs a host sync).
+ * Clipping (hp->max_grad_norm > 0) reads stats->sumsq on the device; with
+ * stats_precomputed the caller may pass statistics summed over all ranks
+ * (the all-reduced flag and sum of squares), which clips to the global norm.
  * Arrays must not overlap one another.  Errors: len < 0, a NULL pointer,
  * step < 1, lr < 0 or not finite, beta not in [0,1), eps <= 0, inv_grad_scale
- * not finite or <= 0, overlapping arrays -> ZERO_ERR_INVALID_ARG; misaligned
+ * not finite or <= 0, max_grad_norm < 0 or not finite, overlapping arrays
+ * -> ZERO_ERR_INVALID_ARG; misaligned
  * pointer -> ZERO_ERR_MISALIGNED; short workspace -> ZERO_ERR_WORKSPACE.
  */
 int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype,

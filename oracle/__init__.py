@@ -75,8 +75,10 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
         for name in ("zo_shard_adam_step_f16", "zo_shard_adam_step_f32"):
             getattr(L, name).argtypes = [_ptr, _ptr, _ptr, _ptr, _ptr, _i64, _i64,
-                                         _dbl, _dbl, _dbl, _dbl, _dbl, _ptr, _ptr]
+                                         _dbl, _dbl, _dbl, _dbl, _dbl, _dbl, _ptr, _ptr]
             getattr(L, name).restype = ctypes.c_int
+        L.zo_clip_factor.argtypes = [_dbl, _dbl]
+        L.zo_clip_factor.restype = _dbl
         _lib = L
     return _lib
 
@@ -167,10 +169,14 @@ def adam_apply(grad, master, m, v, p16, *, step, lr, beta1, beta2, eps,
               beta2, eps, inv_scale, int(overflow))
 
 
+def clip_factor(sumsq: float, max_norm: float) -> float:
+    return lib().zo_clip_factor(sumsq, max_norm)
+
+
 def shard_adam_step(grad, master, m, v, p16, *, step, lr, beta1, beta2, eps,
-                    inv_scale):
-    """Statistics then the gated update, in place.  Returns
-    (status, overflow, sumsq)."""
+                    inv_scale, max_norm=0.0):
+    """Statistics then the gated (and, with max_norm > 0, clipped) update, in
+    place.  Returns (status, overflow, sumsq)."""
     for a, dt in ((master, np.float32), (m, np.float32), (v, np.float32), (p16, np.uint16)):
         _need(a, dt)
     n = master.size
@@ -183,5 +189,5 @@ def shard_adam_step(grad, master, m, v, p16, *, step, lr, beta1, beta2, eps,
         _need(grad, np.float32)
         fn = lib().zo_shard_adam_step_f32
     st = fn(_p(grad), _p(master), _p(m), _p(v), _p(p16), n, step, lr, beta1,
-            beta2, eps, inv_scale, _p(flag), _p(ssq))
+            beta2, eps, inv_scale, max_norm, _p(flag), _p(ssq))
     return st, int(flag[0]), float(ssq[0])

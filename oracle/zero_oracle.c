@@ -192,6 +192,14 @@ int zo_adam_scalars(double lr, double beta1, double beta2, double eps,
   return ZO_OK;
 }
 
+/* [ZS] section 2.1 (global clipping needs the 2-norm over all of P); the
+ * rule itself is a reading, see zero_oracle.h. */
+double zo_clip_factor(double sumsq, double max_norm) {
+  if (!(max_norm > 0.0)) return 1.0;
+  const double norm = sqrt(sumsq);
+  return norm > max_norm ? max_norm / norm : 1.0;
+}
+
 /* [ZS] section 2.1 Fact 1 and [S1M] "Where the 12 bytes come from": the
  * moment updates, the bias-corrected hats, the master-weight step with eps
  * outside the square root, then the fp16 compute copy. */
@@ -241,25 +249,31 @@ int zo_adam_apply_f32(const float *grad, float *master, float *m, float *v,
 int zo_shard_adam_step_f16(const uint16_t *grad, float *master, float *m,
                            float *v, uint16_t *p16, int64_t len, int64_t step,
                            double lr, double beta1, double beta2, double eps,
-                           double inv_scale, uint32_t *overflow,
-                           double *sumsq) {
+                           double inv_scale, double max_norm,
+                           uint32_t *overflow, double *sumsq) {
   float s[9];
-  if (zo_adam_scalars(lr, beta1, beta2, eps, inv_scale, step, s) != ZO_OK)
+  if (zo_adam_scalars(lr, beta1, beta2, eps, inv_scale, step, s) != ZO_OK ||
+      !isfinite(max_norm) || max_norm < 0.0)
     return ZO_ERR_INVALID_ARG;
   zo_grad_stats_f16(grad, len, inv_scale, overflow, sumsq);
+  if (*overflow) return ZO_OK; /* skipped step: nothing is written */
+  const double scale = inv_scale * zo_clip_factor(*sumsq, max_norm);
   return zo_adam_apply_f16(grad, master, m, v, p16, len, step, lr, beta1,
-                           beta2, eps, inv_scale, *overflow);
+                           beta2, eps, scale, 0u);
 }
 
 int zo_shard_adam_step_f32(const float *grad, float *master, float *m,
                            float *v, uint16_t *p16, int64_t len, int64_t step,
                            double lr, double beta1, double beta2, double eps,
-                           double inv_scale, uint32_t *overflow,
-                           double *sumsq) {
+                           double inv_scale, double max_norm,
+                           uint32_t *overflow, double *sumsq) {
   float s[9];
-  if (zo_adam_scalars(lr, beta1, beta2, eps, inv_scale, step, s) != ZO_OK)
+  if (zo_adam_scalars(lr, beta1, beta2, eps, inv_scale, step, s) != ZO_OK ||
+      !isfinite(max_norm) || max_norm < 0.0)
     return ZO_ERR_INVALID_ARG;
   zo_grad_stats_f32(grad, len, inv_scale, overflow, sumsq);
+  if (*overflow) return ZO_OK; /* skipped step: nothing is written */
+  const double scale = inv_scale * zo_clip_factor(*sumsq, max_norm);
   return zo_adam_apply_f32(grad, master, m, v, p16, len, step, lr, beta1,
-                           beta2, eps, inv_scale, *overflow);
+                           beta2, eps, scale, 0u);
 }

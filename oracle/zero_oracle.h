@@ -27,6 +27,8 @@
  *   zo_adam_*               pinned: t=1 closed form, constant-gradient closed forms,
  *                                   pure-decay closed forms, high-precision evaluation,
  *                                   separability and skip invariants
+ *   zo_clip_factor          pinned: the clipped gradient's norm equals max_norm
+ *                                   (exact rational check), no-op below the bound
  */
 #ifndef ZERO_ORACLE_H
 #define ZERO_ORACLE_H
@@ -99,6 +101,15 @@ void zo_grad_stats_f32(const float *grad, int64_t len, double inv_scale,
 int zo_adam_scalars(double lr, double beta1, double beta2, double eps,
                     double inv_scale, int64_t step, float s[9]);
 
+/* Global-norm gradient clipping ([ZS] section 2.1: clipping needs ||g||_2
+ * over all of P, one scalar all-reduce).  The pages do not spell the rule
+ * out; reading: with norm = sqrt(sumsq) of the unscaled gradient, the
+ * gradient is multiplied by max_norm / norm when max_norm > 0 and norm >
+ * max_norm, else left alone.  Returns that factor (1 when not clipping).
+ * The step folds it into the unscale multiplier: s = (float)(inv_scale *
+ * factor), one rounding, computed in double. */
+double zo_clip_factor(double sumsq, double max_norm);
+
 /* One element: g = f32(x)*s; m1 = b1*m + (1-b1)*g; v1 = b2*v + (1-b2)*(g*g);
  * mh = m1/bc1; vh = v1/bc2; th1 = th - lr*(mh/(sqrt(vh)+eps)); p = f16(th1). */
 void zo_adam_element(float x, const float s[9], float *master, float *m,
@@ -115,18 +126,20 @@ int zo_adam_apply_f32(const float *grad, float *master, float *m, float *v,
                       double beta1, double beta2, double eps, double inv_scale,
                       uint32_t overflow);
 
-/* Whole step on a shard: statistics of the gradient, then the gated update.
- * Returns ZO_OK or ZO_ERR_INVALID_ARG; *overflow and *sumsq are outputs.   */
+/* Whole step on a shard: statistics of the gradient, then the gated update
+ * (clipped to max_norm when max_norm > 0, from the shard's own sum of
+ * squares).  Returns ZO_OK or ZO_ERR_INVALID_ARG; *overflow and *sumsq are
+ * outputs.                                                                */
 int zo_shard_adam_step_f16(const uint16_t *grad, float *master, float *m,
                            float *v, uint16_t *p16, int64_t len, int64_t step,
                            double lr, double beta1, double beta2, double eps,
-                           double inv_scale, uint32_t *overflow,
-                           double *sumsq);
+                           double inv_scale, double max_norm,
+                           uint32_t *overflow, double *sumsq);
 int zo_shard_adam_step_f32(const float *grad, float *master, float *m,
                            float *v, uint16_t *p16, int64_t len, int64_t step,
                            double lr, double beta1, double beta2, double eps,
-                           double inv_scale, uint32_t *overflow,
-                           double *sumsq);
+                           double inv_scale, double max_norm,
+                           uint32_t *overflow, double *sumsq);
 
 #ifdef __cplusplus
 }

@@ -88,9 +88,9 @@ def test_workspace_and_status_strings():
         assert lib.zero_status_string(code)
 
 
-def _hp(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8):
+def _hp(lr=1e-4, b1=0.9, b2=0.999, eps=1e-8, mgn=0.0):
     from zero_partitioned_mixed_flat_amd._native import _HParams
-    return _HParams(lr, b1, b2, eps)
+    return _HParams(lr, b1, b2, eps, mgn)
 
 
 A = 1 << 20  # made-up, 16-byte-aligned "device" addresses; never dereferenced
@@ -110,6 +110,7 @@ def _adam(lib, **kw):
     (dict(stats=None), -1), (dict(hp=None), -1), (dict(step=0), -1),
     (dict(hp=_hp(lr=-1.0)), -1), (dict(hp=_hp(b1=1.0)), -1), (dict(hp=_hp(b2=-0.5)), -1),
     (dict(hp=_hp(eps=0.0)), -1), (dict(hp=_hp(lr=float("nan"))), -1), (dict(s=0.0), -1),
+    (dict(hp=_hp(mgn=-1.0)), -1), (dict(hp=_hp(mgn=float("inf"))), -1),
     (dict(s=float("inf")), -1), (dict(m=3 * A + 4), -2), (dict(p16=5 * A + 8), -2),
     (dict(m=2 * A + 64), -1),                       # exp_avg overlaps master
     (dict(pre=0, ws=None), -1), (dict(pre=0, wsn=16), -3), (dict(pre=0, ws=7 * A + 8), -2),

@@ -125,6 +125,64 @@ def test_tiny_workload_end_to_end(dev):
     assert (np.abs(th - closed) <= np.spacing(np.abs(host_f32(master))) / 2 + 8 * 2.0 ** -24 * LR).all()
 
 
+def _stats_tensor(dev, flag, sumsq):
+    """A device zero_grad_stats_t holding given values (e.g. statistics
+    summed over ranks, as an all-reduce would deliver them)."""
+    import struct
+
+    import torch
+    raw = np.frombuffer(struct.pack("<IId", flag, 0, sumsq), dtype=np.uint8).copy()
+    return torch.from_numpy(raw).to(dev)
+
+
+@pytest.mark.parametrize("n,max_norm", [(4097, 0.01), (300_001, 0.1), (300_001, 1e9)])
+def test_clipping_with_given_global_stats(dev, n, max_norm):
+    """Clipping reads the device statistics; given the oracle's own (or the
+    sum over four shards, standing in for the all-reduce), the GPU step is
+    bit-identical to the oracle's."""
+    seed = 3000 + n
+    say(f"adam_step clip n={n} max_norm={max_norm}")
+    master, m, v, p16 = _state(n, seed, False, dev)
+    g = _grad16(n, seed, dev)
+    before = _host_state(master, m, v, p16)
+    g_h = host_u16(g)
+    flag, ssq = oracle.grad_stats(g_h, S16)
+    other = [oracle.grad_stats(host_u16(_grad16(n, seed, dev, stream=tk.STREAM_GRAD + 1 + r)), S16)[1]
+             for r in range(3)]
+    for total in (ssq, ssq + sum(other)):
+        st = _stats_tensor(dev, flag, total)
+        gm, gv, gt, gp = [t.clone() for t in (m, v, master, p16)]
+        zs.adam_step(g, gt, gm, gv, gp, step=7, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16,
+                     max_grad_norm=max_norm, stats=st, stats_precomputed=True)
+        ref = [a.copy() for a in before]
+        scale = S16 * oracle.clip_factor(total, max_norm)
+        assert oracle.adam_apply(g_h, *ref, step=7, lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS,
+                                 inv_scale=scale, overflow=flag) == 0
+        counts = assert_state_parity(_host_state(gt, gm, gv, gp), ref, f"clip n={n}")
+        assert sum(counts.values()) == 0
+
+
+def test_clipping_end_to_end(dev):
+    """Statistics computed by the GPU, clipping active: within the parity bar
+    (the GPU's and the oracle's sums of squares differ by summation order)."""
+    n = 250_003
+    master, m, v, p16 = _state(n, 31, False, dev)
+    g = _grad16(n, 31, dev)
+    before = _host_state(master, m, v, p16)
+    g_h = host_u16(g)
+    stats = zs.new_stats(dev)
+    zs.adam_step(g, master, m, v, p16, step=2, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16,
+                 max_grad_norm=0.05, stats=stats)
+    got_stats = zs.read_stats(stats)
+    ref = [a.copy() for a in before]
+    rc, rflag, rssq = oracle.shard_adam_step(g_h, *ref, step=2, lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS,
+                                             inv_scale=S16, max_norm=0.05)
+    assert rc == 0 and np.sqrt(rssq) > 0.05
+    assert_stats(got_stats, (rflag, rssq), "clip e2e")
+    counts = assert_state_parity(_host_state(master, m, v, p16), ref, "clip e2e")
+    say("  inexact elements:", counts)
+
+
 @pytest.mark.parametrize("n_slices", [1, 2, 3, 8, 9, 17, 64])
 @pytest.mark.parametrize("n", [5, 2048, 2049, 70_001])
 def test_reduce(dev, n_slices, n):

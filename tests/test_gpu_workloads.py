@@ -88,6 +88,35 @@ def test_gpt2xl_shard_full_arrays(dev):
 
 
 @pytest.mark.timeout(600)
+def test_gpt2xl_shard_clipped_sampled(dev):
+    """The GPT-2-XL shard with global-norm clipping at max_norm = 1 (the
+    shard's gradient norm is about 19): compared on a stratified sample, with
+    the device statistics set to the oracle's sum of squares so that the
+    clipping factor is the same on both sides."""
+    import struct
+
+    import torch
+    n = zs.partition_layout(1_500_000_000, 4, 0, 128).shard_len
+    say(f"GPT-2-XL shard, clipped: n={n}")
+    master, m, v, p16 = tk.init_shard_state(n, 0xC2C, zero_moments=False, device=dev)
+    g = _grad16(n, 0xC2C, dev, 1e-3 * 65536)
+    idx = stratified_sample(n, 2_000_000, 0xC2C)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    before = _gather(idx_dev, master, m, v, p16)
+    g_h = host_u16(g)
+    flag, ssq = oracle_stats_full(g_h, S16)
+    assert flag == 0 and np.sqrt(ssq) > 1.0
+    st = torch.from_numpy(np.frombuffer(struct.pack("<IId", flag, 0, ssq), dtype=np.uint8).copy()).to(dev)
+    zs.adam_step(g, master, m, v, p16, step=1000, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16,
+                 max_grad_norm=1.0, stats=st, stats_precomputed=True)
+    after = _gather(idx_dev, master, m, v, p16)
+    ref = [a.copy() for a in before]
+    _apply_sample(g_h[idx], ref, step=1000, s=S16 * oracle.clip_factor(ssq, 1.0), overflow=0)
+    counts = assert_state_parity(after, ref, "gpt2xl clipped sample")
+    assert sum(counts.values()) == 0
+
+
+@pytest.mark.timeout(600)
 def test_7b_n8_shard_sampled_and_inf_run(dev):
     """psi = 7e9, N = 8, rank 0 (875,000,064 params), t = 1000: a clean run
     compared on a stratified sample, then a run with 0.001% of the gradient

@@ -225,6 +225,19 @@ def test_overflow_skip_leaves_state_untouched(orc):
     assert ssq == orc.grad_stats(x16, S16)[1]
 
 
+def test_apply_with_overflow_flag_writes_nothing(orc):
+    rng = np.random.default_rng(14)
+    n = 3000
+    th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32)
+    x16 = _f16(rng.standard_normal(n) * 65.536)
+    got = _apply(orc, x16, th, m, v, 4, overflow=1)
+    for a, b in zip(got[:3], (th, m, v)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert not got[3].any()
+
+
 def test_loss_scale_invariance(orc):
     # only g = x * s enters the update: x * 2^k with s * 2^-k gives the same bits
     rng = np.random.default_rng(12)

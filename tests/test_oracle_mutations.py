@@ -18,6 +18,7 @@ SRC = os.path.join(ROOT, "oracle", "zero_oracle.c")
 ADAM = "tests/test_oracle_adam.py"
 RS = "tests/test_oracle_reduce_stats.py"
 F16 = "tests/test_oracle_f16.py"
+CLIP = "tests/test_oracle_clip.py"
 LM = "tests/test_oracle_layout_memory.py"
 
 MUTATIONS = [
@@ -33,6 +34,7 @@ MUTATIONS = [
     ("lr squared", "s[6] = (float)lr;", "s[6] = (float)(lr * lr);", ADAM),
     ("p16 from the wrong variable", "*p16 = zo_f32_to_f16(th1);", "*p16 = zo_f32_to_f16(mh);", ADAM),
     ("skip ignored", "if (overflow) return ZO_OK; /* skipped", "if (0) return ZO_OK; /* skipped", ADAM),
+    ("whole-step skip ignored", "if (*overflow) return ZO_OK; /* skipped", "if (0) return ZO_OK; /* skipped", ADAM),
     ("1-b in float", "s[1] = (float)(1.0 - beta1);", "s[1] = 1.0f - (float)beta1;", ADAM),
     ("reduce drops slice 0", "float acc = zo_f16_to_f32(slices[0][j]);", "float acc = 0.0f;", RS),
     ("reduce in reverse order",
@@ -47,6 +49,10 @@ MUTATIONS = [
     ("layout floor", "rows = psi / unit + (psi % unit != 0 ? 1 : 0);", "rows = psi / unit;", LM),
     ("layout offset", "const int64_t offset = (int64_t)rank * shard;", "const int64_t offset = (int64_t)rank * (shard - 1);", LM),
     ("memory stage 2", "case 2: return 2.0 * psi + (2.0 * psi + K * psi) / n;", "case 2: return 2.0 * psi + (K * psi) / n;", LM),
+    ("clip norm without sqrt", "const double norm = sqrt(sumsq);", "const double norm = sumsq;", CLIP),
+    ("clip factor inverted", "return norm > max_norm ? max_norm / norm : 1.0;",
+     "return norm > max_norm ? norm / max_norm : 1.0;", CLIP),
+    ("clip below the bound", "return norm > max_norm ? max_norm / norm : 1.0;", "return max_norm / norm;", CLIP),
     ("memory stage 1", "case 1: return 2.0 * psi + 2.0 * psi + K * psi / n;", "case 1: return 2.0 * psi + K * psi / n;", LM),
 ]
 

@@ -48,7 +48,8 @@ class _Layout(ctypes.Structure):
 
 class _HParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
-                ("beta2", ctypes.c_double), ("eps", ctypes.c_double)]
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("max_grad_norm", ctypes.c_double)]
 
 
 _p = ctypes.c_void_p
@@ -199,8 +200,10 @@ def grad_stats(grad, stats, *, inv_grad_scale: float, workspace=None, stream=Non
 
 def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: float,
               betas=(0.9, 0.999), eps: float = 1e-8, inv_grad_scale: float = 1.0,
-              stats, stats_precomputed: bool = False, workspace=None, stream=None) -> None:
-    """One rank's fused Adam step on its shard, in place (see zero_shard.h)."""
+              max_grad_norm: float = 0.0, stats, stats_precomputed: bool = False,
+              workspace=None, stream=None) -> None:
+    """One rank's fused Adam step on its shard, in place (see zero_shard.h);
+    max_grad_norm > 0 clips to that global 2-norm using stats->sumsq."""
     torch = _torch()
     length = master.numel()
     g_p = _dev_ptr(grad, None, "grad", length)
@@ -208,7 +211,7 @@ def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: floa
             _dev_ptr(exp_avg, torch.float32, "exp_avg", length),
             _dev_ptr(exp_avg_sq, torch.float32, "exp_avg_sq", length),
             _dev_ptr(param16, torch.float16, "param16", length)]
-    hp = _HParams(float(lr), float(betas[0]), float(betas[1]), float(eps))
+    hp = _HParams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(max_grad_norm))
     ws_p, ws_n = None, 0
     if not stats_precomputed:
         if workspace is None:

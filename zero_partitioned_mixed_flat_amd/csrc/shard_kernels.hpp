@@ -52,10 +52,22 @@ __device__ __forceinline__ void stream_store(T *p, T v) {
   __builtin_nontemporal_store(v, p);
 }
 
-// Per-step constants, each derived in double on the host and rounded once.
+// Per-step constants, each derived in double on the host and rounded once;
+// inv_scale and max_norm stay in double for the clipping factor, which
+// depends on the device-resident sum of squares.
 struct StepScalars {
   float b1, omb1, b2, omb2, bc1, bc2, lr, eps, s;
+  double inv_scale, max_norm;
 };
+
+// The unscale multiplier of this step: s, or with global-norm clipping
+// active (max_norm > 0 and sqrt(sumsq) > max_norm) the double product
+// inv_scale * (max_norm / sqrt(sumsq)) rounded once to float.
+__device__ __forceinline__ float step_scale(const StepScalars &c, const zero_grad_stats_t *stats) {
+  if (!(c.max_norm > 0.0)) return c.s;
+  const double norm = __builtin_sqrt(stats->sumsq);
+  return norm > c.max_norm ? static_cast<float>(c.inv_scale * (c.max_norm / norm)) : c.s;
+}
 
 // One block's share of the statistics.
 struct Partial {
@@ -92,9 +104,9 @@ __device__ __forceinline__ uint32_t nonfinite_f16x2(uint32_t w) {
 // "ZeRO Stage 1 Math", "Where the 12 bytes come from"): one IEEE binary32
 // operation per operator in the order written, nothing fused.
 __device__ __forceinline__ void adam_element(float x, float &m, float &v, float &th,
-                                             uint32_t &p16, const StepScalars &c) {
+                                             uint32_t &p16, const StepScalars &c, float s) {
 #pragma clang fp contract(off)
-  const float g = x * c.s;
+  const float g = x * s;
   const float m1 = c.b1 * m + c.omb1 * g;
   const float v1 = c.b2 * v + c.omb2 * (g * g);
   const float mh = m1 / c.bc1;
@@ -359,6 +371,7 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     float *__restrict__ v, uint16_t *__restrict__ p16, int64_t len, StepScalars c,
     const zero_grad_stats_t *__restrict__ stats) {
   if (stats->overflow != 0u) return;
+  const float s = step_scale(c, stats);
   constexpr int kSpan = kUpdateBlock * kChunk;  // elements of one chunk row of the block
   constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
@@ -397,7 +410,7 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
         float ta[kChunk] = {tt[k].x, tt[k].y, tt[k].z, tt[k].w};
         uint32_t h[kChunk];
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) adam_element(x[k][e], ma[e], va[e], ta[e], h[e], c);
+        for (int e = 0; e < kChunk; ++e) adam_element(x[k][e], ma[e], va[e], ta[e], h[e], c, s);
         const uint32_t j = lane + k * kSpan;
         stream_store(reinterpret_cast<f32x4 *>(m + tbase + j), f32x4{ma[0], ma[1], ma[2], ma[3]});
         stream_store(reinterpret_cast<f32x4 *>(v + tbase + j), f32x4{va[0], va[1], va[2], va[3]});
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
               x = static_cast<const float *>(grad)[j];
             float mj = m[j], vj = v[j], tj = master[j];
             uint32_t h;
-            adam_element(x, mj, vj, tj, h, c);
+            adam_element(x, mj, vj, tj, h, c, s);
             m[j] = mj;
             v[j] = vj;
             master[j] = tj;

@@ -342,6 +342,8 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
   if (!(std::isfinite(hp->eps) && hp->eps > 0.0)) return fail(ZERO_ERR_INVALID_ARG, "adam_step: eps must be > 0");
   if (!scale_valid(inv_grad_scale))
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: inv_grad_scale must be finite and > 0");
+  if (!(std::isfinite(hp->max_grad_norm) && hp->max_grad_norm >= 0.0))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: max_grad_norm must be finite and >= 0");
   if (len > INT64_MAX / 4) return fail(ZERO_ERR_INT_OVERFLOW, "adam_step: len too large");
   if (!aligned16(grad) || !aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
       !aligned16(param16) || !aligned16(stats))
@@ -370,6 +372,8 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
   c.lr = static_cast<float>(hp->lr);
   c.eps = static_cast<float>(hp->eps);
   c.s = static_cast<float>(inv_grad_scale);
+  c.inv_scale = inv_grad_scale;
+  c.max_norm = hp->max_grad_norm;
 
   int st;
   if (!stats_precomputed) {
