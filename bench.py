@@ -129,6 +129,30 @@ def reduce_secondary(torch, zs, tk, dev, steps):
             "traffic": counter_traffic(REDUCE_COUNTERS_FILE)}
 
 
+def allgather_secondary(torch, zs, tk, dev, steps):
+    """The fp16 all-gather of the GPT-2-XL layout: four 375,000,064-value
+    shards concatenated into the 1.5e9-value flat replica (4 B/param)."""
+    L = zs.partition_layout(PSI, N_RANKS, 0, ALIGN).shard_len
+    shards = [tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 1.0, 0xA6, tk.STREAM_GRAD + r)
+              for r in range(N_RANKS)]
+    replica = torch.empty(PSI, dtype=torch.float16, device=dev)
+    for _ in range(2):
+        zs.allgather(shards, replica)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        zs.allgather(shards, replica)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) * 1e-3 / steps
+    gbps = 4 * PSI / sec / 1e9
+    del shards, replica
+    return {"workload": "fp16 all-gather of the GPT-2-XL layout: 4 shards of 375,000,064 -> 1.5e9-value replica",
+            "ms": round(sec * 1e3, 4), "params_per_s": PSI / sec, "hbm_gbps": round(gbps, 1),
+            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": 4}
+
+
 def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
     """The oracle (single-threaded C, untuned) on the first 2^24 parameters of
     the shard: statistics then the gated update, repeated until ~10 s."""
@@ -254,7 +278,8 @@ def main():
         del ws
         secondary = {"clipped_update": {"max_grad_norm": 1.0, "avg_launch_ms": round(clip_avg, 4),
                                         "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},
-                     "reduce_n64": reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
+                     "reduce_n64": reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2)),
+                     "allgather_gpt2xl": allgather_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
         log(f"secondary: {secondary}")
 
     cpu = None

@@ -153,6 +153,28 @@ int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices,
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * zero_shard_allgather -- the all-gather of the refreshed fp16 shards
+ * ([S1M] "The per-step mechanics", beat 4: every rank broadcasts its fresh
+ * fp16 shard and all ranks end with the identical fp16 model; [ZS] section
+ * 3.1), for N simulated owners whose shard buffers sit in this GPU's memory:
+ * the flat fp16 replica of psi parameters is the concatenation of the shards
+ * in rank order, padding left out.
+ *   shards      host array of n_ranks device pointers, each shard_len fp16
+ *               values (binary16 bit patterns)
+ *   shard_len   the layout's shard_len; a multiple of 8
+ *   psi         number of parameters; replica[r*shard_len + j] = shards[r][j]
+ *               for every r, j with r*shard_len + j < psi
+ *   replica     device [psi] fp16, written
+ * Errors: n_ranks not in [1, ZERO_MAX_SLICES], shard_len < 0 or not a
+ * multiple of 8, psi < 0 or > n_ranks*shard_len, a NULL pointer (psi > 0),
+ * replica overlapping a shard -> ZERO_ERR_INVALID_ARG; misaligned pointer ->
+ * ZERO_ERR_MISALIGNED.
+ */
+int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks,
+                         int64_t shard_len, int64_t psi, uint16_t *replica,
+                         hipStream_t stream);
+
+/*
  * zero_shard_grad_stats -- overflow flag and sum of squares of the shard's
  * gradient.  [ZS] section 2.1: global clipping needs ||g||_2 over all of P,
  * one extra scalar all-reduce; this is the shard-local share.  The overflow

@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = None
         L.zo_grad_reduce.argtypes = [_ptr, _i32, _i64, _ptr]
         L.zo_grad_reduce.restype = None
+        L.zo_allgather.argtypes = [_ptr, _i32, _i64, _i64, _ptr]
+        L.zo_allgather.restype = None
         for name in ("zo_grad_stats_f16", "zo_grad_stats_f32"):
             getattr(L, name).argtypes = [_ptr, _i64, _dbl, _ptr, _ptr]
             getattr(L, name).restype = None
@@ -132,6 +134,19 @@ def grad_reduce(slices) -> np.ndarray:
     ptrs = (ctypes.c_void_p * n)(*[_p(r) for r in rows])
     out = np.empty(length, dtype=np.float32)
     lib().zo_grad_reduce(ctypes.cast(ptrs, ctypes.c_void_p), n, length, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------- all-gather
+def allgather(shards, psi: int) -> np.ndarray:
+    """Flat fp16 replica (uint16 bits, psi elements) from equal-length shards."""
+    rows = [_need(np.asarray(s), np.uint16) for s in shards]
+    n = len(rows)
+    length = rows[0].size
+    assert all(r.size == length for r in rows) and psi <= n * length
+    ptrs = (ctypes.c_void_p * n)(*[_p(r) for r in rows])
+    out = np.empty(psi, dtype=np.uint16)
+    lib().zo_allgather(ctypes.cast(ptrs, ctypes.c_void_p), n, length, psi, _p(out))
     return out
 
 

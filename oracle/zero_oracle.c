@@ -126,6 +126,19 @@ void zo_grad_reduce(const uint16_t *const *slices, int32_t n_slices,
   }
 }
 
+/* --------------------------------------------------------------- all-gather */
+
+/* [S1M] "The per-step mechanics" beat 4: the flat fp16 replica is the
+ * concatenation of the ranks' shards in rank order, padding left out. */
+void zo_allgather(const uint16_t *const *shards, int32_t n_ranks,
+                  int64_t shard_len, int64_t psi, uint16_t *replica) {
+  for (int32_t r = 0; r < n_ranks; ++r)
+    for (int64_t j = 0; j < shard_len; ++j) {
+      const int64_t flat = (int64_t)r * shard_len + j;
+      if (flat < psi) replica[flat] = shards[r][j];
+    }
+}
+
 /* ------------------------------------------------------------------- stats */
 
 /* Neumaier's compensated summation: sum + comp is the running total. */

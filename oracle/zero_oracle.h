@@ -23,6 +23,8 @@
  *   zo_f32_to_f16           pinned: exhaustive over 2^32 codes vs numpy / F16C
  *   zo_grad_reduce          pinned: exact integer sums, identity at N=1, fp32 error bound,
  *                                   hand-worked order-dependent case
+ *   zo_allgather            pinned: numpy concatenation of the real parts, scatter/gather
+ *                                   round trip through the partition layout
  *   zo_grad_stats_*         pinned: injected-inf counts, exact rational sum of squares
  *   zo_adam_*               pinned: t=1 closed form, constant-gradient closed forms,
  *                                   pure-decay closed forms, high-precision evaluation,
@@ -77,6 +79,15 @@ void zo_f32_to_f16_array(const float *in, uint16_t *out, int64_t n);
  * f32(slices[0][j]) + f32(slices[1][j]) + ... in rank order.               */
 void zo_grad_reduce(const uint16_t *const *slices, int32_t n_slices,
                     int64_t len, float *out);
+
+/* ---- all-gather of the refreshed fp16 shards ---------------------------
+ * [S1M] "The per-step mechanics" beat 4 and [ZS] section 3.1: every rank's
+ * fresh fp16 shard is gathered so all ranks hold the identical full fp16
+ * model.  On one GPU: the N shard buffers (shard_len each) are concatenated
+ * into the flat replica of psi parameters; element j of rank r lands at
+ * r*shard_len + j when that is below psi (padding is not copied).         */
+void zo_allgather(const uint16_t *const *shards, int32_t n_ranks,
+                  int64_t shard_len, int64_t psi, uint16_t *replica);
 
 /* ---- gradient statistics: overflow flag and sum of squares ------------
  * [ZS] section 2.1 (global clipping needs ||g||_2 over all of P, one scalar

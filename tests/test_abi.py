@@ -145,6 +145,22 @@ def test_reduce_and_stats_reject_bad_arguments():
     assert g(A + 2, 1, 5, 1.0, 2 * A, 3 * A, 1 << 16, None) == -2
 
 
+def test_allgather_rejects_bad_arguments():
+    lib = zs.library()
+    ptrs = (ctypes.c_void_p * 65)(*[A * (i + 1) for i in range(65)])
+    rep = 100 * A
+    f = lib.zero_shard_allgather
+    assert f(ptrs, 0, 64, 10, rep, None) == -1          # no shards
+    assert f(ptrs, 65, 64, 10, rep, None) == -1         # too many
+    assert f(ptrs, 4, 60, 10, rep, None) == -1          # shard_len not a multiple of 8
+    assert f(ptrs, 4, 64, 257, rep, None) == -1         # psi beyond N*shard_len
+    assert f(ptrs, 4, 64, -1, rep, None) == -1
+    assert f(ptrs, 4, 64, 200, rep + 2, None) == -2     # misaligned replica
+    assert f(ptrs, 4, 64, 200, A, None) == -1           # replica overlaps shard 0
+    bad = (ctypes.c_void_p * 2)(A, A + 2)
+    assert f(bad, 2, 64, 100, rep, None) == -2          # misaligned shard
+
+
 def test_philox_known_answers():
     # Known-answer vectors published with the Random123 Philox4x32-10
     # reference implementation (Salmon et al., SC'11).

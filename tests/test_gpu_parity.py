@@ -219,6 +219,22 @@ def test_reduce_many_partials(dev):
     assert zs.read_stats(stats)[0] == 1
 
 
+@pytest.mark.parametrize("psi,n_ranks", [(1, 1), (1000, 4), (1_000_003, 4), (1_048_576, 4), (777_777, 64),
+                                          (5000, 64), (4095, 3)])
+def test_allgather(dev, psi, n_ranks):
+    """The flat fp16 replica from N shards: ragged last shards, empty shards
+    (psi small against N), N = 64."""
+    import torch
+    lay = zs.partition_layout(psi, n_ranks, 0, 128)
+    L = lay.shard_len
+    say(f"allgather psi={psi} N={n_ranks} shard_len={L}")
+    shards = [_grad16(L, psi, dev, stream=tk.STREAM_GRAD + r) for r in range(n_ranks)]
+    replica = torch.empty(psi, dtype=torch.float16, device=dev)
+    zs.allgather(shards, replica)
+    ref = oracle.allgather([host_u16(t) for t in shards], psi)
+    assert np.array_equal(host_u16(replica), ref)
+
+
 @pytest.mark.parametrize("special", [np.inf, -np.inf, np.nan])
 def test_reduce_flags_nonfinite_slice(dev, special):
     import torch

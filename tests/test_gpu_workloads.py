@@ -117,6 +117,22 @@ def test_gpt2xl_shard_clipped_sampled(dev):
 
 
 @pytest.mark.timeout(600)
+def test_gpt2xl_allgather_full(dev):
+    """The flat fp16 replica of psi = 1.5e9 from the four ranks' 375,000,064
+    shards (the last ends with 256 padding values, not copied); every element
+    compared."""
+    import torch
+    psi, N = 1_500_000_000, 4
+    L = zs.partition_layout(psi, N, 0, 128).shard_len
+    say(f"allgather psi={psi} N={N} shard_len={L}")
+    shards = [_grad16(L, 0xA6, dev, 1.0, tk.STREAM_GRAD + r) for r in range(N)]
+    replica = torch.empty(psi, dtype=torch.float16, device=dev)
+    zs.allgather(shards, replica)
+    ref = oracle.allgather([host_u16(t) for t in shards], psi)
+    assert np.array_equal(host_u16(replica), ref)
+
+
+@pytest.mark.timeout(600)
 def test_7b_n8_shard_sampled_and_inf_run(dev):
     """psi = 7e9, N = 8, rank 0 (875,000,064 params), t = 1000: a clean run
     compared on a stratified sample, then a run with 0.001% of the gradient

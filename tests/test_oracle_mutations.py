@@ -19,6 +19,7 @@ ADAM = "tests/test_oracle_adam.py"
 RS = "tests/test_oracle_reduce_stats.py"
 F16 = "tests/test_oracle_f16.py"
 CLIP = "tests/test_oracle_clip.py"
+AG = "tests/test_oracle_allgather.py"
 LM = "tests/test_oracle_layout_memory.py"
 
 MUTATIONS = [
@@ -53,6 +54,10 @@ MUTATIONS = [
     ("clip factor inverted", "return norm > max_norm ? max_norm / norm : 1.0;",
      "return norm > max_norm ? norm / max_norm : 1.0;", CLIP),
     ("clip below the bound", "return norm > max_norm ? max_norm / norm : 1.0;", "return max_norm / norm;", CLIP),
+    ("allgather rank order reversed", "if (flat < psi) replica[flat] = shards[r][j];",
+     "if (flat < psi) replica[flat] = shards[n_ranks - 1 - r][j];", AG),
+    ("allgather offset stride", "const int64_t flat = (int64_t)r * shard_len + j;",
+     "const int64_t flat = (int64_t)r * (shard_len - (shard_len > 1)) + j;", AG),
     ("memory stage 1", "case 1: return 2.0 * psi + 2.0 * psi + K * psi / n;", "case 1: return 2.0 * psi + K * psi / n;", LM),
 ]
 

@@ -8,17 +8,18 @@ Stages 1, 2, and 3 Explained", "DeepSpeed ZeRO: Extreme Memory Efficiency"):
 * ``grad_reduce``       -- owner-side fp32 sum of N fp16 gradient slices
 * ``grad_stats``        -- overflow flag and sum of squares of the gradient
 * ``adam_step``         -- fused fp32 Adam update of master/m/v + fp16 copy
+* ``allgather``         -- the flat fp16 replica from the N owners' shards
 
 All device work runs in the HIP library ``libzero_shard.so`` (C ABI in
 ``include/zero_shard.h``); this package only marshals arguments.
 """
 from ._native import (  # noqa: F401
-    STATS_BYTES, ZERO_F16, ZERO_F32, ZERO_MAX_SLICES, Layout, ZeroError, adam_step,
+    STATS_BYTES, ZERO_F16, ZERO_F32, ZERO_MAX_SLICES, Layout, ZeroError, adam_step, allgather,
     grad_reduce, grad_stats, library, model_state_bytes, new_stats, new_workspace,
     partition_layout, read_stats, workspace_bytes)
 
 __all__ = [
     "Layout", "ZeroError", "partition_layout", "model_state_bytes", "workspace_bytes",
-    "new_workspace", "new_stats", "read_stats", "grad_reduce", "grad_stats", "adam_step",
+    "new_workspace", "new_stats", "read_stats", "grad_reduce", "grad_stats", "adam_step", "allgather",
     "library", "ZERO_F16", "ZERO_F32", "ZERO_MAX_SLICES", "STATS_BYTES",
 ]

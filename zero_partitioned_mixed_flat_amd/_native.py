@@ -63,6 +63,8 @@ _lib.zero_workspace_bytes.argtypes = [_i64]
 _lib.zero_workspace_bytes.restype = _sz
 _lib.zero_shard_grad_reduce.argtypes = [_p, _i32, _i64, _p, _p, _dbl, _p, _sz, _p]
 _lib.zero_shard_grad_reduce.restype = ctypes.c_int
+_lib.zero_shard_allgather.argtypes = [_p, _i32, _i64, _i64, _p, _p]
+_lib.zero_shard_allgather.restype = ctypes.c_int
 _lib.zero_shard_grad_stats.argtypes = [_p, ctypes.c_int, _i64, _dbl, _p, _p, _sz, _p]
 _lib.zero_shard_grad_stats.restype = ctypes.c_int
 _lib.zero_shard_adam_step.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _i64, _i64,
@@ -186,6 +188,20 @@ def grad_reduce(slices: Sequence, out, *, stats=None, inv_grad_scale: float = 1.
         ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
     _check(_lib.zero_shard_grad_reduce(ctypes.cast(ptrs, ctypes.c_void_p), n, length, out_p, stats_p,
                                        float(inv_grad_scale), ws_p, ws_n, _stream(stream)))
+
+
+def allgather(shards: Sequence, replica, *, stream=None) -> None:
+    """replica (fp16, psi elements) = the shards (fp16, equal lengths, rank
+    order) concatenated without the padding beyond psi."""
+    torch = _torch()
+    n = len(shards)
+    if not 1 <= n <= ZERO_MAX_SLICES:
+        raise ValueError(f"need 1..{ZERO_MAX_SLICES} shards, got {n}")
+    shard_len = shards[0].numel()
+    ptrs = (ctypes.c_void_p * n)(*[_dev_ptr(s, torch.float16, f"shards[{i}]", shard_len)
+                                   for i, s in enumerate(shards)])
+    _check(_lib.zero_shard_allgather(ctypes.cast(ptrs, ctypes.c_void_p), n, shard_len, replica.numel(),
+                                     _dev_ptr(replica, torch.float16, "replica"), _stream(stream)))
 
 
 def grad_stats(grad, stats, *, inv_grad_scale: float, workspace=None, stream=None) -> None:

@@ -324,6 +324,36 @@ int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices, int6
   return ok();
 }
 
+int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks, int64_t shard_len, int64_t psi,
+                         uint16_t *replica, hipStream_t stream) {
+  if (n_ranks < 1 || n_ranks > ZERO_MAX_SLICES)
+    return fail(ZERO_ERR_INVALID_ARG, "allgather: n_ranks must be in [1, %d]", ZERO_MAX_SLICES);
+  if (shard_len < 0 || shard_len % 8 != 0)
+    return fail(ZERO_ERR_INVALID_ARG, "allgather: shard_len must be a non-negative multiple of 8");
+  if (shard_len > INT64_MAX / ZERO_MAX_SLICES / 2) return fail(ZERO_ERR_INT_OVERFLOW, "allgather: shard_len too large");
+  if (psi < 0 || psi > shard_len * n_ranks) return fail(ZERO_ERR_INVALID_ARG, "allgather: psi out of range");
+  if (shards == nullptr || (replica == nullptr && psi > 0)) return fail(ZERO_ERR_INVALID_ARG, "allgather: NULL pointer");
+  if (!aligned16(replica)) return fail(ZERO_ERR_MISALIGNED, "allgather: replica misaligned");
+  zs::SliceTable tab{};
+  for (int r = 0; r < n_ranks; ++r) {
+    const int64_t first = static_cast<int64_t>(r) * shard_len;
+    const int64_t real = psi - first < shard_len ? (psi - first > 0 ? psi - first : 0) : shard_len;
+    if (shards[r] == nullptr && real > 0) return fail(ZERO_ERR_INVALID_ARG, "allgather: shard %d is NULL", r);
+    if (!aligned16(shards[r])) return fail(ZERO_ERR_MISALIGNED, "allgather: shard %d misaligned", r);
+    if (overlap(shards[r], static_cast<size_t>(shard_len) * 2, replica, static_cast<size_t>(psi) * 2))
+      return fail(ZERO_ERR_INVALID_ARG, "allgather: replica overlaps shard %d", r);
+    tab.p[r] = shards[r];
+  }
+  if (psi == 0 || shard_len == 0) return ok();
+  const int64_t tiles = ceil_div(shard_len, zs::kGatherTile);
+  if (tiles > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "allgather: shard_len too large");
+  clear_stale_error();
+  zs::allgather_kernel<<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(n_ranks)), zs::kGatherBlock, 0,
+                         stream>>>(tab, shard_len, psi, replica);
+  const int st = check_launch("allgather_kernel");
+  return st == ZERO_OK ? ok() : st;
+}
+
 int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
                          float *exp_avg, float *exp_avg_sq, uint16_t *param16, int64_t len, int64_t step,
                          const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
