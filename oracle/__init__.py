@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.zo_grad_reduce.restype = None
         L.zo_allgather.argtypes = [_ptr, _i32, _i64, _i64, _ptr]
         L.zo_allgather.restype = None
+        L.zo_qwz_quantize.argtypes = [_ptr, _i64, _ptr, _ptr]
+        L.zo_qwz_quantize.restype = None
+        L.zo_qwz_dequantize.argtypes = [_ptr, _ptr, _i64, _ptr]
+        L.zo_qwz_dequantize.restype = None
         for name in ("zo_grad_stats_f16", "zo_grad_stats_f32"):
             getattr(L, name).argtypes = [_ptr, _i64, _dbl, _ptr, _ptr]
             getattr(L, name).restype = None
@@ -147,6 +151,28 @@ def allgather(shards, psi: int) -> np.ndarray:
     ptrs = (ctypes.c_void_p * n)(*[_p(r) for r in rows])
     out = np.empty(psi, dtype=np.uint16)
     lib().zo_allgather(ctypes.cast(ptrs, ctypes.c_void_p), n, length, psi, _p(out))
+    return out
+
+
+# ------------------------------------------------------------------------ qwZ
+QWZ_BLOCK = 256
+
+
+def qwz_quantize(x16: np.ndarray):
+    """(codes int8[len], scales float32[ceil(len/256)]) of fp16 bits."""
+    x16 = _need(np.ascontiguousarray(x16), np.uint16)
+    codes = np.empty(x16.size, dtype=np.int8)
+    scales = np.empty(-(-x16.size // QWZ_BLOCK), dtype=np.float32)
+    lib().zo_qwz_quantize(_p(x16), x16.size, _p(codes), _p(scales))
+    return codes, scales
+
+
+def qwz_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = _need(np.ascontiguousarray(codes), np.int8)
+    scales = _need(np.ascontiguousarray(scales), np.float32)
+    assert scales.size == -(-codes.size // QWZ_BLOCK)
+    out = np.empty(codes.size, dtype=np.uint16)
+    lib().zo_qwz_dequantize(_p(codes), _p(scales), codes.size, _p(out))
     return out
 
 

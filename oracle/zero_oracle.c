@@ -139,6 +139,38 @@ void zo_allgather(const uint16_t *const *shards, int32_t n_ranks,
     }
 }
 
+/* --------------------------------------------------------------------- qwZ */
+
+/* [ZS] section 5.3 qwZ; the block rule is a reading (zero_oracle.h). */
+void zo_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes,
+                     float *scales) {
+  for (int64_t lo = 0; lo < len; lo += ZO_QWZ_BLOCK) {
+    const int64_t hi = (lo + ZO_QWZ_BLOCK < len) ? lo + ZO_QWZ_BLOCK : len;
+    float amax = 0.0f;
+    for (int64_t j = lo; j < hi; ++j) {
+      const float a = fabsf(zo_f16_to_f32(x16[j]));
+      if (a > amax) amax = a;
+    }
+    const float scale = amax / 127.0f;
+    scales[lo / ZO_QWZ_BLOCK] = scale;
+    for (int64_t j = lo; j < hi; ++j) {
+      float q = 0.0f;
+      if (scale != 0.0f) {
+        q = rintf(zo_f16_to_f32(x16[j]) / scale); /* ties to even */
+        if (q > 127.0f) q = 127.0f;
+        if (q < -127.0f) q = -127.0f;
+      }
+      codes[j] = (int8_t)q;
+    }
+  }
+}
+
+void zo_qwz_dequantize(const int8_t *codes, const float *scales, int64_t len,
+                       uint16_t *out16) {
+  for (int64_t j = 0; j < len; ++j)
+    out16[j] = zo_f32_to_f16((float)codes[j] * scales[j / ZO_QWZ_BLOCK]);
+}
+
 /* ------------------------------------------------------------------- stats */
 
 /* Neumaier's compensated summation: sum + comp is the running total. */

@@ -25,6 +25,8 @@
  *                                   hand-worked order-dependent case
  *   zo_allgather            pinned: numpy concatenation of the real parts, scatter/gather
  *                                   round trip through the partition layout
+ *   zo_qwz_*                pinned: exact multiples of a power-of-two scale, ties to even,
+ *                                   zero blocks, the +-127 extremes, round-trip error bound
  *   zo_grad_stats_*         pinned: injected-inf counts, exact rational sum of squares
  *   zo_adam_*               pinned: t=1 closed form, constant-gradient closed forms,
  *                                   pure-decay closed forms, high-precision evaluation,
@@ -88,6 +90,22 @@ void zo_grad_reduce(const uint16_t *const *slices, int32_t n_slices,
  * r*shard_len + j when that is below psi (padding is not copied).         */
 void zo_allgather(const uint16_t *const *shards, int32_t n_ranks,
                   int64_t shard_len, int64_t psi, uint16_t *replica);
+
+/* ---- qwZ: block INT8 quantization of the outgoing fp16 weights --------
+ * [ZS] section 5.3 (qwZ: fp16 weights sent as INT8 with per-block scales)
+ * and the ZeRO++ discussion of [ZOS] (small blocks, each with its own scale;
+ * dequantized back to fp16 on receipt).  Block size, scale and rounding are
+ * not on the pages; reading: blocks of ZO_QWZ_BLOCK consecutive values of the
+ * flat shard, symmetric scale = max|x| / 127 (binary32), code =
+ * clamp(rint(x / scale), -127, 127) with x / scale one correctly rounded
+ * binary32 division and rint ties-to-even; a block whose max is 0 has scale
+ * 0 and all codes 0.  Dequantization: f16(code * scale), one binary32
+ * product then round-to-nearest-even.  Inputs are finite fp16 values.      */
+#define ZO_QWZ_BLOCK 256
+void zo_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes,
+                     float *scales);
+void zo_qwz_dequantize(const int8_t *codes, const float *scales, int64_t len,
+                       uint16_t *out16);
 
 /* ---- gradient statistics: overflow flag and sum of squares ------------
  * [ZS] section 2.1 (global clipping needs ||g||_2 over all of P, one scalar

@@ -20,6 +20,7 @@ RS = "tests/test_oracle_reduce_stats.py"
 F16 = "tests/test_oracle_f16.py"
 CLIP = "tests/test_oracle_clip.py"
 AG = "tests/test_oracle_allgather.py"
+QWZ = "tests/test_oracle_qwz.py"
 LM = "tests/test_oracle_layout_memory.py"
 
 MUTATIONS = [
@@ -58,6 +59,12 @@ MUTATIONS = [
      "if (flat < psi) replica[flat] = shards[n_ranks - 1 - r][j];", AG),
     ("allgather offset stride", "const int64_t flat = (int64_t)r * shard_len + j;",
      "const int64_t flat = (int64_t)r * (shard_len - (shard_len > 1)) + j;", AG),
+    ("qwz truncates", "q = rintf(zo_f16_to_f32(x16[j]) / scale); /* ties to even */",
+     "q = truncf(zo_f16_to_f32(x16[j]) / scale); /* ties to even */", QWZ),
+    ("qwz rounds half away", "q = rintf(zo_f16_to_f32(x16[j]) / scale); /* ties to even */",
+     "q = roundf(zo_f16_to_f32(x16[j]) / scale); /* ties to even */", QWZ),
+    ("qwz scale 255", "const float scale = amax / 127.0f;", "const float scale = amax / 255.0f;", QWZ),
+    ("qwz dequant wrong block", "scales[j / ZO_QWZ_BLOCK]", "scales[j / (ZO_QWZ_BLOCK / 2) / 2 + (j % 2)]", QWZ),
     ("memory stage 1", "case 1: return 2.0 * psi + 2.0 * psi + K * psi / n;", "case 1: return 2.0 * psi + K * psi / n;", LM),
 ]
 
