@@ -16,9 +16,11 @@ parameter for the whole call (2 for the statistics pass, 28 for the update).
 
 Also reported: the update kernel alone against the HBM roofline (HIP events
 around each launch, on the launch stream), a plain copy/read kernel as the
-attainable ceiling, the owner-side reduce of 64 fp16 slices of the 7.5B /
-N = 64 shard (117,187,584 parameters), and the CPU oracle timed on a bounded
-sample of the same workload on one host core.
+attainable ceiling, the update with global-norm clipping, the owner-side
+reduce of 64 fp16 slices of the 7.5B / N = 64 shard (117,187,584
+parameters), the fp16 all-gather and the qwZ block-INT8 variants (encoder
+fused into the update, encoder alone, decoding all-gather), and the CPU
+oracle timed on a bounded sample of the same workload on one host core.
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ PEAK_HBM_GBPS = 8000.0
 UPDATE_BYTES_PER_PARAM = 28      # read g2 m4 v4 th4, write m4 v4 th4 p16 2
 STATS_BYTES_PER_PARAM = 2        # read g2
 REDUCE_BYTES_PER_PARAM = lambda n: 2 * n + 4   # noqa: E731
+QWZ_BYTES_PER_PARAM = 1 + 4 / 256               # int8 code + one fp32 scale per 256 values
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_update_gpt2xl_shard_counters.txt")
 REDUCE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "grad_reduce_7p5b_n64_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc", f)
@@ -151,6 +154,71 @@ def allgather_secondary(torch, zs, tk, dev, steps):
     return {"workload": "fp16 all-gather of the GPT-2-XL layout: 4 shards of 375,000,064 -> 1.5e9-value replica",
             "ms": round(sec * 1e3, 4), "params_per_s": PSI / sec, "hbm_gbps": round(gbps, 1),
             "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": 4}
+
+
+def _avg_ms(torch, fn, steps):
+    """Mean duration of `fn`'s device work, HIP events on the current stream."""
+    evs = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+
+def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, t0):
+    """qwZ block-INT8 weights (blocks of 256, one fp32 scale each): the update
+    with the encoder fused into its write-back, the encoder alone on the fp16
+    shard, and the decoding all-gather of the GPT-2-XL layout."""
+    L = master.numel()
+    codes = torch.empty(L, dtype=torch.int8, device=dev)
+    scales = torch.empty(zs.qwz_scales_len(L), dtype=torch.float32, device=dev)
+    step = [t0]
+
+    def fused():
+        zs.adam_step(g, master, m, v, p16, step=step[0], lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
+                     stats=stats, stats_precomputed=True, qwz_codes=codes, qwz_scales=scales)
+        step[0] += 1
+    fused()
+    fused_ms = _avg_ms(torch, fused, steps)
+    fused_bytes = UPDATE_BYTES_PER_PARAM + QWZ_BYTES_PER_PARAM
+    enc = lambda: zs.qwz_quantize(p16, codes, scales)  # noqa: E731
+    enc()
+    enc_ms = _avg_ms(torch, enc, steps)
+    enc_bytes = 2 + QWZ_BYTES_PER_PARAM
+    del codes, scales
+    torch.cuda.empty_cache()
+
+    all_codes, all_scales = [], []
+    for r in range(N_RANKS):
+        x = tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 0.02, 0xA7, tk.STREAM_MASTER + r)
+        all_codes.append(torch.empty(L, dtype=torch.int8, device=dev))
+        all_scales.append(torch.empty(zs.qwz_scales_len(L), dtype=torch.float32, device=dev))
+        zs.qwz_quantize(x, all_codes[-1], all_scales[-1])
+        del x
+    replica = torch.empty(PSI, dtype=torch.float16, device=dev)
+    gat = lambda: zs.qwz_allgather(all_codes, all_scales, replica)  # noqa: E731
+    gat()
+    gat_ms = _avg_ms(torch, gat, steps)
+    gat_bytes = QWZ_BYTES_PER_PARAM + 2
+    del all_codes, all_scales, replica
+    torch.cuda.empty_cache()
+
+    def entry(workload, ms, n, bytes_per):
+        gbps = bytes_per * n / (ms * 1e-3) / 1e9
+        return {"workload": workload, "avg_launch_ms": round(ms, 4), "params_per_s": n / (ms * 1e-3),
+                "hbm_gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                "bytes_per_param": bytes_per}
+    return {
+        "update_fused": entry("GPT-2-XL shard update with qwZ encoding of the fresh fp16 weights",
+                              fused_ms, L, fused_bytes),
+        "quantize_shard": entry("qwZ encoding of the 375,000,064-value fp16 shard", enc_ms, L, enc_bytes),
+        "allgather_gpt2xl": entry("qwZ all-gather of the GPT-2-XL layout: 4 encoded shards -> 1.5e9-value "
+                                  "fp16 replica", gat_ms, PSI, gat_bytes),
+    }
 
 
 def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
@@ -275,9 +343,12 @@ def main():
             clip_ms.append((a, b))
         torch.cuda.synchronize()
         clip_avg = sum(a.elapsed_time(b) for a, b in clip_ms) / len(clip_ms)
+        zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
+        qwz = qwz_secondary(torch, zs, tk, dev, args.steps, g, master, m, v, p16, stats, T0 + 200)
         del ws
         secondary = {"clipped_update": {"max_grad_norm": 1.0, "avg_launch_ms": round(clip_avg, 4),
                                         "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},
+                     "qwz": qwz,
                      "reduce_n64": reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2)),
                      "allgather_gpt2xl": allgather_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
         log(f"secondary: {secondary}")

@@ -1,8 +1,9 @@
 /*
  * zero_shard.h -- C ABI of the per-rank ZeRO shard optimizer step on one
  * MI355X (gfx950): the partition of the flat parameter space, the owner-side
- * gradient reduce, the gradient statistics and the fused mixed-precision Adam
- * update of one rank's owned partition.
+ * gradient reduce, the gradient statistics, the fused mixed-precision Adam
+ * update of one rank's owned partition, the all-gather of the fp16 shards and
+ * its block-INT8 (qwZ) variant.
  *
  * Sources, cited by page title and section:
  *   [ZS]  "DeepSpeed ZeRO Stages"
@@ -40,9 +41,11 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 2
+#define ZERO_SHARD_ABI_VERSION 3
 /* Largest number of simulated rank slices one reduce call accepts. */
 #define ZERO_MAX_SLICES 64
+/* Values per qwZ quantization block (one binary32 scale each). */
+#define ZERO_QWZ_BLOCK 256
 
 typedef enum {
   ZERO_OK = 0,
@@ -234,6 +237,71 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype,
                          int64_t step, const zero_adam_hparams_t *hp,
                          zero_grad_stats_t *stats, int32_t stats_precomputed,
                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * zero_shard_adam_step_qwz -- zero_shard_adam_step that also encodes the
+ * fresh fp16 shard for a quantized all-gather ([ZS] section 5.3, qwZ: the
+ * fp16 weights travel as INT8 with one scale per block; [ZOS] ZeRO++: small
+ * blocks with their own scale factors, dequantized to fp16 on receipt).
+ * Same arguments, semantics and errors as zero_shard_adam_step, plus
+ *   codes    device int8 [len], written: codes[j] = clamp(rint(f32(param16[j])
+ *            / scale_b), -127, 127) for j in block b = j / ZERO_QWZ_BLOCK
+ *            (0 when scale_b is 0)
+ *   scales   device fp32 [ceil(len / ZERO_QWZ_BLOCK)], written: scale_b =
+ *            max over the block of |f32(param16[j])| / 127
+ * Blocks start at element 0 of the shard; the last may be short.  The codes
+ * are those of zero_qwz_quantize applied to the param16 this call writes,
+ * computed while the values are still in registers (1 + 4/256 bytes more per
+ * parameter instead of a second pass of 3 + 4/256).  On overflow nothing is
+ * written, codes and scales included.  Codes of a block holding a non-finite
+ * fp16 weight are unspecified.  codes and scales must not overlap each other
+ * or the other arrays.
+ */
+int zero_shard_adam_step_qwz(const void *grad, zero_dtype_t grad_dtype,
+                             double inv_grad_scale, float *master,
+                             float *exp_avg, float *exp_avg_sq,
+                             uint16_t *param16, int8_t *codes, float *scales,
+                             int64_t len, int64_t step,
+                             const zero_adam_hparams_t *hp,
+                             zero_grad_stats_t *stats,
+                             int32_t stats_precomputed, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * zero_qwz_quantize -- the qwZ encoder on its own ([ZS] section 5.3; [ZOS]
+ * ZeRO++): blocks of ZERO_QWZ_BLOCK consecutive values from element 0, the
+ * last possibly short; scale_b = max|x| / 127 in binary32 and code =
+ * clamp(rint(x / scale_b), -127, 127) with one correctly rounded division and
+ * ties to even, all codes 0 when scale_b is 0.
+ *   x16      device fp16 [len] (binary16 bit patterns), finite values; codes
+ *            of a block holding +-inf or NaN are unspecified
+ *   codes    device int8 [len], written
+ *   scales   device fp32 [ceil(len / ZERO_QWZ_BLOCK)], written
+ * Errors: len < 0, a NULL pointer (len > 0), overlapping arrays ->
+ * ZERO_ERR_INVALID_ARG; misaligned pointer -> ZERO_ERR_MISALIGNED.
+ */
+int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes,
+                      float *scales, hipStream_t stream);
+
+/*
+ * zero_qwz_allgather -- receiver side of the quantized all-gather ([ZS]
+ * section 5.3, qwZ; [ZOS] ZeRO++: received INT8 weights are dequantized back
+ * to fp16 before use): the N owners' encoded shards, already in this GPU's
+ * memory, are decoded into the flat fp16 replica:
+ *   replica[r*shard_len + j] = f16(f32(codes[r][j]) * scales[r][j / 256])
+ * (one binary32 product, round to nearest even) for every r, j with
+ * r*shard_len + j < psi; padding is not written.
+ *   codes, scales   host arrays of n_ranks device pointers: shard_len int8
+ *                   codes and ceil(shard_len / 256) fp32 scales per rank,
+ *                   as zero_qwz_quantize or zero_shard_adam_step_qwz write
+ *   shard_len       the layout's shard_len; a multiple of 8
+ *   replica         device [psi] fp16, written
+ * Errors as for zero_shard_allgather.
+ */
+int zero_qwz_allgather(const int8_t *const *codes,
+                       const float *const *scales, int32_t n_ranks,
+                       int64_t shard_len, int64_t psi, uint16_t *replica,
+                       hipStream_t stream);
 
 /* Static text for a status code. */
 const char *zero_status_string(int status);

@@ -141,3 +141,39 @@ def stratified_sample(n, count, seed, edge=4096):
     idx = np.arange(count, dtype=np.int64) * stride + rng.integers(0, stride, count)
     idx = np.concatenate([np.arange(min(edge, n)), idx, np.arange(max(0, n - edge), n)])
     return np.unique(idx[idx < n])
+
+
+def oracle_qwz_quantize_full(x16):
+    """The oracle's qwZ encoding of a large fp16 array, on chunks whose
+    boundaries are multiples of 1024 (so every block lies in one chunk)."""
+    import numpy as np
+
+    import oracle
+    n = x16.size
+    codes = np.empty(n, dtype=np.int8)
+    scales = np.empty(-(-n // oracle.QWZ_BLOCK), dtype=np.float32)
+
+    def run(ab):
+        a, b = ab
+        c, s = oracle.qwz_quantize(x16[a:b])
+        codes[a:b] = c
+        scales[a // oracle.QWZ_BLOCK:a // oracle.QWZ_BLOCK + s.size] = s
+    with _cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(run, _chunks(n, 4 * THREADS)))
+    return codes, scales
+
+
+def oracle_qwz_dequantize_full(codes, scales):
+    import numpy as np
+
+    import oracle
+    n = codes.size
+    out = np.empty(n, dtype=np.uint16)
+
+    def run(ab):
+        a, b = ab
+        blk = a // oracle.QWZ_BLOCK
+        out[a:b] = oracle.qwz_dequantize(codes[a:b], scales[blk:blk + -(-(b - a) // oracle.QWZ_BLOCK)])
+    with _cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(run, _chunks(n, 4 * THREADS)))
+    return out

@@ -37,6 +37,7 @@ def test_shard_header_declares_the_path():
     names = set(_declared(os.path.join(ROOT, "include", "zero_shard.h")))
     assert {"zero_partition_layout", "zero_model_state_bytes", "zero_workspace_bytes",
             "zero_shard_grad_reduce", "zero_shard_grad_stats", "zero_shard_adam_step",
+            "zero_shard_allgather", "zero_shard_adam_step_qwz", "zero_qwz_quantize", "zero_qwz_allgather",
             "zero_status_string", "zero_last_error"} <= names
 
 
@@ -159,6 +160,58 @@ def test_allgather_rejects_bad_arguments():
     assert f(ptrs, 4, 64, 200, A, None) == -1           # replica overlaps shard 0
     bad = (ctypes.c_void_p * 2)(A, A + 2)
     assert f(bad, 2, 64, 100, rep, None) == -2          # misaligned shard
+
+
+def _adam_qwz(lib, codes=8 * A, scales=9 * A, **kw):
+    a = dict(grad=A, dt=1, s=1.0, master=2 * A, m=3 * A, v=4 * A, p16=5 * A, n=1000, step=1,
+             hp=_hp(), stats=6 * A, pre=1, ws=7 * A, wsn=1 << 16)
+    a.update(kw)
+    return lib.zero_shard_adam_step_qwz(a["grad"], a["dt"], a["s"], a["master"], a["m"], a["v"], a["p16"], codes,
+                                        scales, a["n"], a["step"], ctypes.byref(a["hp"]), a["stats"], a["pre"],
+                                        a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(codes=None), -1), (dict(scales=None), -1), (dict(codes=8 * A + 4), -2), (dict(scales=9 * A + 8), -2),
+    (dict(codes=5 * A + 512), -1),                  # codes overlap param16
+    (dict(scales=8 * A + 992), -1),                 # scales overlap codes (1000 bytes)
+    (dict(n=-1), -1), (dict(step=0), -1), (dict(m=3 * A + 4), -2),
+])
+def test_adam_step_qwz_rejects_bad_arguments(kw, status):
+    lib = zs.library()
+    assert _adam_qwz(lib, **kw) == status
+    assert lib.zero_last_error()
+
+
+def test_qwz_quantize_and_allgather_reject_bad_arguments():
+    lib = zs.library()
+    q = lib.zero_qwz_quantize
+    assert q(A, -1, 2 * A, 3 * A, None) == -1
+    assert q(None, 10, 2 * A, 3 * A, None) == -1
+    assert q(A, 10, None, 3 * A, None) == -1
+    assert q(A, 10, 2 * A, None, None) == -1
+    assert q(A + 2, 10, 2 * A, 3 * A, None) == -2
+    assert q(A, 10, 2 * A + 4, 3 * A, None) == -2
+    assert q(A, 1000, A + 1024, 3 * A, None) == -1     # codes inside x16 (2000 bytes)
+    assert q(A, 1000, 2 * A, 2 * A + 992, None) == -1  # scales overlap codes
+    assert q(A, 0, None, None, None) == 0              # empty: nothing to do, no device call
+    codes = (ctypes.c_void_p * 65)(*[A * (i + 1) for i in range(65)])
+    scales = (ctypes.c_void_p * 65)(*[A * (i + 101) for i in range(65)])
+    rep = 300 * A
+    g = lib.zero_qwz_allgather
+    assert g(codes, scales, 0, 64, 10, rep, None) == -1
+    assert g(codes, scales, 65, 64, 10, rep, None) == -1
+    assert g(codes, scales, 4, 60, 10, rep, None) == -1      # shard_len not a multiple of 8
+    assert g(codes, scales, 4, 64, 257, rep, None) == -1     # psi beyond N*shard_len
+    assert g(codes, None, 4, 64, 10, rep, None) == -1
+    assert g(codes, scales, 4, 64, 200, rep + 2, None) == -2
+    assert g(codes, scales, 4, 64, 200, A, None) == -1       # replica overlaps codes of shard 0
+    assert g(codes, scales, 4, 64, 200, 101 * A, None) == -1  # replica overlaps scales of shard 0
+    bad = (ctypes.c_void_p * 2)(A, A + 4)
+    assert g(bad, scales, 2, 64, 100, rep, None) == -2
+    assert g(codes, scales, 4, 64, 0, rep, None) == 0        # psi = 0: nothing to do
+    assert zs.qwz_scales_len(0) == 0 and zs.qwz_scales_len(1) == 1 and zs.qwz_scales_len(256) == 1
+    assert zs.qwz_scales_len(257) == 2 and zs.ZERO_QWZ_BLOCK == 256
 
 
 def test_philox_known_answers():

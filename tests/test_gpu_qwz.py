@@ -1,0 +1,225 @@
+"""GPU parity of the qwZ block-INT8 codec ("DeepSpeed ZeRO Stages" 5.3, qwZ;
+ZeRO++ in "ZeRO Optimization: Stages 1, 2, and 3 Explained") against the
+oracle: the standalone encoder, the encoder fused into the Adam update's
+write-back, and the decoding all-gather.  Codes, scales and decoded fp16
+values are integer decisions or single correctly rounded operations, so the
+bar is bit-exact everywhere; the update's own outputs keep the step's bar."""
+import numpy as np
+import pytest
+
+import oracle
+import zero_partitioned_mixed_flat_amd as zs
+from zero_partitioned_mixed_flat_amd import testkit as tk
+from gpu_util import assert_state_parity, assert_stats, host_f32, host_u16, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+LR, BETAS, EPS = 1e-4, (0.9, 0.999), 1e-8
+S16 = 2.0 ** -16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _f16_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16)).to(dev)
+
+
+def _encode(x, dev):
+    import torch
+    n = x.numel()
+    codes = torch.empty(n, dtype=torch.int8, device=dev)
+    scales = torch.empty(zs.qwz_scales_len(n), dtype=torch.float32, device=dev)
+    zs.qwz_quantize(x, codes, scales)
+    return codes, scales
+
+
+def _assert_codec(codes, scales, ref, name):
+    rc, rs = ref
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), f"{name}: scales differ"
+    bad = np.flatnonzero(gc != rc)
+    assert bad.size == 0, f"{name}: {bad.size} codes differ; first at {bad[0]}: {gc[bad[0]]} vs {rc[bad[0]]}"
+
+
+def _structured(n, seed):
+    """fp16 weights with the cases the codec has to get right: N(0, 0.02)
+    bulk, all-zero blocks, a lone outlier per block, blocks of subnormals,
+    +-65504, and exact ties x = (k + 1/2) * scale with a power-of-two scale."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * 0.02).astype(np.float16)
+    nb = -(-n // 256)
+    for b in range(nb):
+        lo, hi = b * 256, min(n, b * 256 + 256)
+        kind = b % 7
+        if kind == 1:
+            x[lo:hi] = 0
+        elif kind == 2:
+            x[lo + rng.integers(0, hi - lo)] = np.float16(rng.choice([-1, 1]) * 3.75)
+        elif kind == 3:
+            x[lo:hi] = (rng.integers(-1023, 1024, hi - lo) * 2.0 ** -24).astype(np.float16)
+        elif kind == 4:
+            x[lo] = np.float16(65504.0)
+            if hi - lo > 1:
+                x[hi - 1] = np.float16(-65504.0)
+        elif kind == 5:
+            # max |x| = 127 * 2^-6 -> scale 2^-6; ties at (k + 1/2) * 2^-6
+            k = rng.integers(-126, 126, hi - lo)
+            x[lo:hi] = ((k + 0.5) * 2.0 ** -6).astype(np.float16)
+            x[lo] = np.float16(-127 * 2.0 ** -6)
+    return x.view(np.uint16)
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 255, 256, 257, 1023, 1024, 1025, 4097, 65536 + 13, 1_000_003])
+def test_quantize(dev, n):
+    say(f"qwz_quantize n={n}")
+    x = _structured(n, n)
+    codes, scales = _encode(_f16_dev(x, dev), dev)
+    _assert_codec(codes, scales, oracle.qwz_quantize(x), f"quantize n={n}")
+
+
+@pytest.mark.parametrize("sigma", [1e-3, 0.02, 1.0, 300.0])
+def test_quantize_normal_weights(dev, sigma):
+    import torch
+    n = 300_001
+    say(f"qwz_quantize normal sigma={sigma}")
+    x = tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), sigma, 0x51, tk.STREAM_MASTER)
+    codes, scales = _encode(x, dev)
+    ref = oracle.qwz_quantize(host_u16(x))
+    _assert_codec(codes, scales, ref, f"quantize sigma={sigma}")
+    assert np.abs(ref[0]).max() == 127
+
+
+def _fused_step(g, master, m, v, p16, *, step, s, max_norm=0.0):
+    import torch
+    n = master.numel()
+    codes = torch.full((n,), 77, dtype=torch.int8, device=g.device)
+    scales = torch.full((zs.qwz_scales_len(n),), -1.0, dtype=torch.float32, device=g.device)
+    stats = zs.new_stats(g.device)
+    zs.adam_step(g, master, m, v, p16, step=step, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s,
+                 max_grad_norm=max_norm, stats=stats, qwz_codes=codes, qwz_scales=scales)
+    return codes, scales, zs.read_stats(stats)
+
+
+@pytest.mark.parametrize("n", [1, 5, 255, 256, 257, 511, 512, 513, 4097, 100_003, 1_000_003])
+@pytest.mark.parametrize("gdt", ["f16", "f32"])
+def test_fused_step(dev, n, gdt):
+    """The update with the encoder in its write-back: state within the step's
+    bar, codes and scales bit-exact with the oracle's encoding of the
+    oracle's fp16 weights; the plain update gives the same state bits."""
+    import torch
+    say(f"adam_step_qwz n={n} grad={gdt}")
+    master, m, v, p16 = tk.init_shard_state(n, 0x9A + n, zero_moments=False, device=dev)
+    if gdt == "f16":
+        g = tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), 1e-3 * 65536, n, tk.STREAM_GRAD)
+        g_h, s = host_u16(g), S16
+    else:
+        g = tk.normal_f32_(torch.empty(n, dtype=torch.float32, device=dev), 0.0, 1e-3, n, tk.STREAM_GRAD)
+        g_h, s = host_f32(g), 1.0
+    before = [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
+    twin = [t.clone() for t in (master, m, v, p16)]
+    codes, scales, got_stats = _fused_step(g, master, m, v, p16, step=7, s=s)
+    ref = [a.copy() for a in before]
+    rc, rflag, rssq = oracle.shard_adam_step(g_h, *ref, step=7, lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS,
+                                             inv_scale=s)
+    assert rc == 0 and rflag == 0
+    assert_stats(got_stats, (rflag, rssq), f"qwz n={n}")
+    counts = assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref, f"qwz n={n}")
+    assert sum(counts.values()) == 0
+    _assert_codec(codes, scales, oracle.qwz_quantize(ref[3]), f"fused n={n}")
+    stats = zs.new_stats(dev)
+    zs.adam_step(g, *twin, step=7, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s, stats=stats)
+    for a, b in zip(twin, (master, m, v, p16)):
+        assert torch.equal(a.view(torch.int16) if a.element_size() == 2 else a.view(torch.int32),
+                           b.view(torch.int16) if b.element_size() == 2 else b.view(torch.int32))
+
+
+def test_fused_step_clipped(dev):
+    import torch
+    n = 200_003
+    say(f"adam_step_qwz clipped n={n}")
+    master, m, v, p16 = tk.init_shard_state(n, 0x9C, zero_moments=False, device=dev)
+    g = tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), 1e-3 * 65536, 0x9C, tk.STREAM_GRAD)
+    ref = [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
+    g_h = host_u16(g)
+    codes, scales, got_stats = _fused_step(g, master, m, v, p16, step=3, s=S16, max_norm=0.05)
+    rc, rflag, rssq = oracle.shard_adam_step(g_h, *ref, step=3, lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS,
+                                             inv_scale=S16, max_norm=0.05)
+    assert rc == 0 and np.sqrt(rssq) > 0.05
+    assert_stats(got_stats, (rflag, rssq), "qwz clipped")
+    assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref, "qwz clipped")
+    _assert_codec(codes, scales, oracle.qwz_quantize(ref[3]), "fused clipped")
+
+
+def test_fused_step_skips_on_overflow(dev):
+    """An overflowing gradient skips the step: no state, codes or scales
+    are written."""
+    import torch
+    n = 70_001
+    master, m, v, p16 = tk.init_shard_state(n, 0x9D, zero_moments=False, device=dev)
+    g = tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), 1e-3 * 65536, 0x9D, tk.STREAM_GRAD)
+    g[n - 2] = float("inf")
+    before = [t.clone() for t in (master, m, v, p16)]
+    codes, scales, got_stats = _fused_step(g, master, m, v, p16, step=2, s=S16)
+    assert got_stats[0] == 1
+    for a, b in zip(before, (master, m, v, p16)):
+        assert torch.equal(a, b)
+    assert bool((codes == 77).all()) and bool((scales == -1.0).all())
+
+
+def test_zero_length(dev):
+    import torch
+    e16 = torch.empty(0, dtype=torch.float16, device=dev)
+    codes, scales = _encode(e16, dev)
+    assert codes.numel() == 0 and scales.numel() == 0
+    e32 = torch.empty(0, dtype=torch.float32, device=dev)
+    c0, s0 = torch.empty(0, dtype=torch.int8, device=dev), torch.empty(0, dtype=torch.float32, device=dev)
+    stats = zs.new_stats(dev)
+    zs.adam_step(e16, e32, e32.clone(), e32.clone(), e16.clone(), step=1, lr=LR, stats=stats,
+                 qwz_codes=c0, qwz_scales=s0)
+    assert zs.read_stats(stats) == (0, 0.0)
+    zs.qwz_allgather([c0], [s0], torch.empty(0, dtype=torch.float16, device=dev))
+
+
+@pytest.mark.parametrize("psi,n_ranks", [(1, 1), (1000, 4), (1_000_003, 4), (1_048_576, 4), (777_777, 64),
+                                          (5000, 64), (4095, 3)])
+def test_allgather(dev, psi, n_ranks):
+    """Decoding gather: encoded shards from the encoder (checked against the
+    oracle), replica against the oracle's decode-then-concatenate; ragged
+    last shards, shards that lie wholly in the padding, N = 64."""
+    import torch
+    L = zs.partition_layout(psi, n_ranks, 0, 128).shard_len
+    say(f"qwz_allgather psi={psi} N={n_ranks} shard_len={L}")
+    shards_h = [_structured(L, 1000 * psi + r) for r in range(n_ranks)]
+    enc = [_encode(_f16_dev(x, dev), dev) for x in shards_h]
+    ref_enc = [oracle.qwz_quantize(x) for x in shards_h]
+    for r, ((c, s), ref) in enumerate(zip(enc, ref_enc)):
+        _assert_codec(c, s, ref, f"shard {r}")
+    replica = torch.full((psi,), 7.0, dtype=torch.float16, device=dev)
+    zs.qwz_allgather([c for c, _ in enc], [s for _, s in enc], replica)
+    ref = oracle.allgather([oracle.qwz_dequantize(c, s) for c, s in ref_enc], psi)
+    assert np.array_equal(host_u16(replica), ref)
+
+
+def test_round_trip_bound_on_device_output(dev):
+    """Property at any size: the decoded weight is within half a scale (plus
+    half an fp16 ulp of the result) of the weight, and each block's largest
+    weight decodes from code +-127."""
+    import torch
+    n = 1 << 20
+    x = tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), 0.02, 0x77, tk.STREAM_MASTER)
+    codes, scales = _encode(x, dev)
+    replica = torch.empty(n, dtype=torch.float16, device=dev)
+    zs.qwz_allgather([codes], [scales], replica)
+    xf = x.double().cpu().numpy()
+    back = replica.double().cpu().numpy()
+    sc = np.repeat(scales.double().cpu().numpy(), 256)
+    half_ulp = np.spacing(np.abs(back).astype(np.float16)).astype(np.float64) / 2
+    assert (np.abs(back - xf) <= sc / 2 * (1 + 2.0 ** -20) + half_ulp).all()
+    blocks = np.abs(xf).reshape(-1, 256)
+    top = np.abs(codes.cpu().numpy().astype(np.int64)).reshape(-1, 256)[np.arange(blocks.shape[0]),
+                                                                         blocks.argmax(1)]
+    assert (top == 127).all()

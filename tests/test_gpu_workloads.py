@@ -15,7 +15,8 @@ import oracle
 import zero_partitioned_mixed_flat_amd as zs
 from zero_partitioned_mixed_flat_amd import testkit as tk
 from gpu_util import (assert_state_parity, assert_stats, host_f32, host_u16, oracle_apply_full,
-                      oracle_reduce_full, oracle_stats_full, require_gpu, say, stratified_sample)
+                      oracle_qwz_dequantize_full, oracle_qwz_quantize_full, oracle_reduce_full,
+                      oracle_stats_full, require_gpu, say, stratified_sample)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +130,67 @@ def test_gpt2xl_allgather_full(dev):
     replica = torch.empty(psi, dtype=torch.float16, device=dev)
     zs.allgather(shards, replica)
     ref = oracle.allgather([host_u16(t) for t in shards], psi)
+    assert np.array_equal(host_u16(replica), ref)
+
+
+@pytest.mark.timeout(600)
+def test_gpt2xl_shard_qwz_full_arrays(dev):
+    """The GPT-2-XL shard's update with the qwZ encoder fused into the
+    write-back (the benchmark's launch: statistics, then the update with
+    them precomputed); every state element, code and scale compared with
+    the oracle's step followed by the oracle's encoding."""
+    import torch
+    n = zs.partition_layout(1_500_000_000, 4, 0, 128).shard_len
+    say(f"GPT-2-XL shard, fused qwZ: n={n}, generating")
+    master, m, v, p16 = tk.init_shard_state(n, 0xC2F, zero_moments=False, device=dev)
+    g = _grad16(n, 0xC2F, dev, 1e-3 * 65536)
+    torch.cuda.synchronize()
+    g_h = host_u16(g)
+    ref = [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
+    stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+    codes = torch.empty(n, dtype=torch.int8, device=dev)
+    scales = torch.empty(zs.qwz_scales_len(n), dtype=torch.float32, device=dev)
+    say("  GPU step")
+    zs.grad_stats(g, stats, inv_grad_scale=S16, workspace=ws)
+    zs.adam_step(g, master, m, v, p16, step=1000, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16,
+                 stats=stats, stats_precomputed=True, qwz_codes=codes, qwz_scales=scales)
+    got_stats = zs.read_stats(stats)
+    say("  oracle step and encoding")
+    ref_stats = oracle_stats_full(g_h, S16)
+    assert_stats(got_stats, ref_stats, "gpt2xl qwz")
+    oracle_apply_full(g_h, *ref, step=1000, lr=LR, betas=BETAS, eps=EPS, s=S16, overflow=ref_stats[0])
+    rc, rs = oracle_qwz_quantize_full(ref[3])
+    say("  compare")
+    counts = assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref, "gpt2xl qwz")
+    assert sum(counts.values()) == 0
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.timeout(600)
+def test_gpt2xl_qwz_allgather_full(dev):
+    """The quantized all-gather of psi = 1.5e9 from the four ranks' encoded
+    375,000,064 shards: every code, scale and replica element compared."""
+    import torch
+    psi, N = 1_500_000_000, 4
+    L = zs.partition_layout(psi, N, 0, 128).shard_len
+    say(f"qwz allgather psi={psi} N={N} shard_len={L}")
+    codes, scales, ref_dec = [], [], []
+    for r in range(N):
+        x = tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 0.02, 0xA7, tk.STREAM_MASTER + r)
+        c = torch.empty(L, dtype=torch.int8, device=dev)
+        s = torch.empty(zs.qwz_scales_len(L), dtype=torch.float32, device=dev)
+        zs.qwz_quantize(x, c, s)
+        rc, rs = oracle_qwz_quantize_full(host_u16(x))
+        del x
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(c.cpu().numpy(), rc)
+        ref_dec.append(oracle_qwz_dequantize_full(rc, rs))
+        codes.append(c)
+        scales.append(s)
+    replica = torch.empty(psi, dtype=torch.float16, device=dev)
+    zs.qwz_allgather(codes, scales, replica)
+    ref = oracle.allgather(ref_dec, psi)
     assert np.array_equal(host_u16(replica), ref)
 
 

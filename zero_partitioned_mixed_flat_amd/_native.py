@@ -37,6 +37,7 @@ ZERO_ERR_INT_OVERFLOW = -5
 ZERO_F16 = 1
 ZERO_F32 = 2
 ZERO_MAX_SLICES = 64
+ZERO_QWZ_BLOCK = 256
 STATS_BYTES = 16
 
 
@@ -70,6 +71,13 @@ _lib.zero_shard_grad_stats.restype = ctypes.c_int
 _lib.zero_shard_adam_step.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _i64, _i64,
                                       ctypes.POINTER(_HParams), _p, _i32, _p, _sz, _p]
 _lib.zero_shard_adam_step.restype = ctypes.c_int
+_lib.zero_shard_adam_step_qwz.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _p, _p, _i64, _i64,
+                                          ctypes.POINTER(_HParams), _p, _i32, _p, _sz, _p]
+_lib.zero_shard_adam_step_qwz.restype = ctypes.c_int
+_lib.zero_qwz_quantize.argtypes = [_p, _i64, _p, _p, _p]
+_lib.zero_qwz_quantize.restype = ctypes.c_int
+_lib.zero_qwz_allgather.argtypes = [_p, _p, _i32, _i64, _i64, _p, _p]
+_lib.zero_qwz_allgather.restype = ctypes.c_int
 _lib.zero_status_string.argtypes = [ctypes.c_int]
 _lib.zero_status_string.restype = ctypes.c_char_p
 _lib.zero_last_error.argtypes = []
@@ -217,9 +225,11 @@ def grad_stats(grad, stats, *, inv_grad_scale: float, workspace=None, stream=Non
 def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: float,
               betas=(0.9, 0.999), eps: float = 1e-8, inv_grad_scale: float = 1.0,
               max_grad_norm: float = 0.0, stats, stats_precomputed: bool = False,
-              workspace=None, stream=None) -> None:
+              workspace=None, qwz_codes=None, qwz_scales=None, stream=None) -> None:
     """One rank's fused Adam step on its shard, in place (see zero_shard.h);
-    max_grad_norm > 0 clips to that global 2-norm using stats->sumsq."""
+    max_grad_norm > 0 clips to that global 2-norm using stats->sumsq.  With
+    qwz_codes (int8 [len]) and qwz_scales (fp32 [qwz_scales_len(len)]) the
+    fresh fp16 shard is also block-INT8 encoded in the same pass."""
     torch = _torch()
     length = master.numel()
     g_p = _dev_ptr(grad, None, "grad", length)
@@ -233,6 +243,43 @@ def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: floa
         if workspace is None:
             workspace = new_workspace(length, master.device)
         ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
-    _check(_lib.zero_shard_adam_step(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, length, int(step),
-                                     ctypes.byref(hp), _dev_ptr(stats, None, "stats"), int(bool(stats_precomputed)),
-                                     ws_p, ws_n, _stream(stream)))
+    tail = (length, int(step), ctypes.byref(hp), _dev_ptr(stats, None, "stats"), int(bool(stats_precomputed)),
+            ws_p, ws_n, _stream(stream))
+    if (qwz_codes is None) != (qwz_scales is None):
+        raise ValueError("qwz_codes and qwz_scales go together")
+    if qwz_codes is None:
+        _check(_lib.zero_shard_adam_step(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *tail))
+    else:
+        q = [_dev_ptr(qwz_codes, torch.int8, "qwz_codes", length),
+             _dev_ptr(qwz_scales, torch.float32, "qwz_scales", qwz_scales_len(length))]
+        _check(_lib.zero_shard_adam_step_qwz(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *q, *tail))
+
+
+def qwz_scales_len(length: int) -> int:
+    """Number of qwZ blocks (one fp32 scale each) of `length` values."""
+    return -(-int(length) // ZERO_QWZ_BLOCK)
+
+
+def qwz_quantize(x16, codes, scales, *, stream=None) -> None:
+    """Block-INT8 encoding of fp16 x16 into codes (int8) and scales (fp32)."""
+    torch = _torch()
+    length = x16.numel()
+    _check(_lib.zero_qwz_quantize(_dev_ptr(x16, torch.float16, "x16"), length,
+                                  _dev_ptr(codes, torch.int8, "codes", length),
+                                  _dev_ptr(scales, torch.float32, "scales", qwz_scales_len(length)),
+                                  _stream(stream)))
+
+
+def qwz_allgather(codes: Sequence, scales: Sequence, replica, *, stream=None) -> None:
+    """replica (fp16, psi elements) = the decoded shards (int8 codes and fp32
+    scales per rank, rank order) concatenated without the padding."""
+    torch = _torch()
+    n = len(codes)
+    if not 1 <= n <= ZERO_MAX_SLICES or len(scales) != n:
+        raise ValueError(f"need 1..{ZERO_MAX_SLICES} code and scale buffers, got {n} and {len(scales)}")
+    shard_len = codes[0].numel()
+    cp = (ctypes.c_void_p * n)(*[_dev_ptr(c, torch.int8, f"codes[{i}]", shard_len) for i, c in enumerate(codes)])
+    sp = (ctypes.c_void_p * n)(*[_dev_ptr(s, torch.float32, f"scales[{i}]", qwz_scales_len(shard_len))
+                                 for i, s in enumerate(scales)])
+    _check(_lib.zero_qwz_allgather(ctypes.cast(cp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p), n, shard_len,
+                                   replica.numel(), _dev_ptr(replica, torch.float16, "replica"), _stream(stream)))

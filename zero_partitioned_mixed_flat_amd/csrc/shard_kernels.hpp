@@ -42,6 +42,7 @@ constexpr int kFold = kBlock * 16;  // partials folded by one block of the first
 // Native vector types for the non-temporal load/store builtins.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
@@ -363,11 +364,9 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
 // Concatenation of N fp16 shards into the flat replica: block (x, y) copies
 // tile x of shard y, 16 bytes (8 values) per lane with non-temporal access;
 // only the part of the shard below psi is copied.
-constexpr int kGatherBlock = 256;
-constexpr int kGatherU = 2;
+constexpr int kGatherBlock = 64;
+constexpr int kGatherU = 1;
 constexpr int64_t kGatherTile = static_cast<int64_t>(kGatherBlock) * 8 * kGatherU;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 __global__ __launch_bounds__(kGatherBlock) void allgather_kernel(SliceTable tab, int64_t shard_len, int64_t psi,
                                                                  uint16_t *__restrict__ replica) {
   const int r = blockIdx.y;
@@ -391,17 +390,148 @@ __global__ __launch_bounds__(kGatherBlock) void allgather_kernel(SliceTable tab,
   }
 }
 
+// ----------------------------------------------------------------------- qwZ
+// Block INT8 codec of the fp16 weights ("DeepSpeed ZeRO Stages" 5.3, qwZ;
+// ZeRO++ in "ZeRO Optimization: Stages 1, 2, and 3 Explained"): blocks of
+// kQwzBlock consecutive values of a shard, scale = max|x| / 127 in binary32,
+// code = clamp(rint(x / scale), -127, 127) with a correctly rounded division
+// and ties to even, all codes 0 when the scale is 0; decoding is
+// f16(code * scale).  One row of a wave (64 lanes x 4 values) is exactly one
+// block, so each block maximum is one wave reduction.
+constexpr int kQwzBlock = ZERO_QWZ_BLOCK;
+static_assert(kQwzBlock == kWave * kChunk, "a qwZ block is one wave row");
+
+__device__ __forceinline__ float wave_max(float a) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off, kWave));
+  return a;
+}
+
+__device__ __forceinline__ uint32_t qwz_code(float x, float scale) {
+  float q = __builtin_rintf(x / scale);
+  q = q > 127.0f ? 127.0f : q;
+  q = q < -127.0f ? -127.0f : q;
+  return static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xFFu;
+}
+
+// Scale of the block held by one wave row, from the lane's 4 values (0 for
+// values outside the array), and the lane's 4 codes packed little-endian.
+__device__ __forceinline__ float qwz_scale(const float (&x)[kChunk]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kChunk; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(x[e]));
+  return wave_max(a) / 127.0f;
+}
+
+__device__ __forceinline__ uint32_t qwz_pack(const float (&x)[kChunk], float scale) {
+  if (scale == 0.0f) return 0u;
+  uint32_t w = 0u;
+#pragma unroll
+  for (int e = 0; e < kChunk; ++e) w |= qwz_code(x[e], scale) << (8 * e);
+  return w;
+}
+
+__device__ __forceinline__ uint32_t qwz_decode(uint32_t code8, float scale) {
+  return f2h(static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(code8))) * scale);
+}
+
+// Standalone encoder: fp16 [len] -> codes [len], scales [ceil(len/256)].
+// One wave per block, U rows (blocks) per tile, one tile per block.
+template <int U>
+__global__ __launch_bounds__(kWave) void qwz_quantize_kernel(const uint16_t *__restrict__ x16, int64_t len,
+                                                             uint8_t *__restrict__ codes,
+                                                             float *__restrict__ scales) {
+  constexpr int64_t kTile = static_cast<int64_t>(kQwzBlock) * U;
+  const int64_t ntiles = (len + kTile - 1) / kTile;
+  const uint32_t lane = threadIdx.x * kChunk;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t tbase = tile * kTile;
+    if (tbase + kTile <= len) {
+      u32x2 raw[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) raw[k] = stream_load(reinterpret_cast<const u32x2 *>(x16 + tbase + lane + k * kQwzBlock));
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const float x[kChunk] = {h2f(raw[k].x & 0xFFFFu), h2f(raw[k].x >> 16), h2f(raw[k].y & 0xFFFFu),
+                                 h2f(raw[k].y >> 16)};
+        const float scale = qwz_scale(x);
+        stream_store(reinterpret_cast<uint32_t *>(codes + tbase + lane + k * kQwzBlock), qwz_pack(x, scale));
+        if (threadIdx.x == 0) scales[(tbase + k * kQwzBlock) / kQwzBlock] = scale;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t j0 = tbase + lane + k * kQwzBlock;
+        float x[kChunk];
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) x[e] = j0 + e < len ? h2f(x16[j0 + e]) : 0.0f;
+        const float scale = qwz_scale(x);
+        const uint32_t w = qwz_pack(x, scale);
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e)
+          if (j0 + e < len) codes[j0 + e] = static_cast<uint8_t>(w >> (8 * e));
+        if (threadIdx.x == 0 && tbase + k * kQwzBlock < len) scales[(tbase + k * kQwzBlock) / kQwzBlock] = scale;
+      }
+    }
+  }
+}
+
+// Receiver side of the quantized all-gather: the N owners' code and scale
+// buffers are decoded into the flat fp16 replica; block (x, y) decodes tile
+// x of shard y, only the part of the shard below psi.
+struct QwzTable {
+  const uint8_t *codes[ZERO_MAX_SLICES];
+  const float *scales[ZERO_MAX_SLICES];
+};
+
+template <int U>
+__global__ __launch_bounds__(kWave) void qwz_allgather_kernel(QwzTable tab, int64_t shard_len, int64_t psi,
+                                                              uint16_t *__restrict__ replica) {
+  constexpr int64_t kTile = static_cast<int64_t>(kQwzBlock) * U;
+  const int r = blockIdx.y;
+  const int64_t first = static_cast<int64_t>(r) * shard_len;
+  const int64_t real = psi - first < shard_len ? psi - first : shard_len;
+  const int64_t tbase = static_cast<int64_t>(blockIdx.x) * kTile;
+  if (tbase >= real) return;
+  const uint8_t *src = tab.codes[r] + tbase;
+  const float *sc = tab.scales[r] + tbase / kQwzBlock;
+  uint16_t *dst = replica + first + tbase;
+  const uint32_t lane = threadIdx.x * kChunk;
+  if (tbase + kTile <= real) {
+    uint32_t w[U];
+    float scale[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      w[k] = stream_load(reinterpret_cast<const uint32_t *>(src + lane + k * kQwzBlock));
+      scale[k] = sc[k];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint32_t h0 = qwz_decode(w[k], scale[k]), h1 = qwz_decode(w[k] >> 8, scale[k]);
+      const uint32_t h2 = qwz_decode(w[k] >> 16, scale[k]), h3 = qwz_decode(w[k] >> 24, scale[k]);
+      stream_store(reinterpret_cast<u32x2 *>(dst + lane + k * kQwzBlock), u32x2{h0 | (h1 << 16), h2 | (h3 << 16)});
+    }
+  } else {
+    const int64_t rem = real - tbase;
+    for (int64_t j = threadIdx.x; j < rem; j += kWave) dst[j] = static_cast<uint16_t>(qwz_decode(src[j], sc[j / kQwzBlock]));
+  }
+}
+
 // ---------------------------------------------------------------- the update
 // Fused single pass over the shard: read g, m, v, master; write m, v, master
 // and the fp16 copy (28 B per parameter with an fp16 gradient, 30 B with
-// fp32).  Every block first reads the device-resident overflow flag and
+// fp32).  With QWZ the fresh fp16 values are also encoded (codes and
+// per-block scales, 1 + 4/256 B more per parameter) while still in
+// registers.  Every block first reads the device-resident overflow flag and
 // leaves before any memory access to the states if it is set.  Launched with
 // one block (one wave) per tile of kUpdateBlock*4*U elements.
-template <zero_dtype_t DT, int U>
+template <zero_dtype_t DT, int U, bool QWZ = false>
 __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     const void *__restrict__ grad, float *__restrict__ master, float *__restrict__ m,
     float *__restrict__ v, uint16_t *__restrict__ p16, int64_t len, StepScalars c,
-    const zero_grad_stats_t *__restrict__ stats) {
+    const zero_grad_stats_t *__restrict__ stats, uint8_t *__restrict__ codes = nullptr,
+    float *__restrict__ scales = nullptr) {
+  static_assert(!QWZ || kUpdateBlock * kChunk == kQwzBlock, "one chunk row per qwZ block");
   if (stats->overflow != 0u) return;
   const float s = step_scale(c, stats);
   constexpr int kSpan = kUpdateBlock * kChunk;  // elements of one chunk row of the block
@@ -448,14 +578,22 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
         stream_store(reinterpret_cast<f32x4 *>(v + tbase + j), f32x4{va[0], va[1], va[2], va[3]});
         stream_store(reinterpret_cast<f32x4 *>(master + tbase + j), f32x4{ta[0], ta[1], ta[2], ta[3]});
         stream_store(reinterpret_cast<u32x2 *>(p16 + tbase + j), u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        if constexpr (QWZ) {
+          const float w[kChunk] = {h2f(h[0]), h2f(h[1]), h2f(h[2]), h2f(h[3])};
+          const float scale = qwz_scale(w);
+          stream_store(reinterpret_cast<uint32_t *>(codes + tbase + j), qwz_pack(w, scale));
+          if (threadIdx.x == 0) scales[(tbase + k * kSpan) / kQwzBlock] = scale;
+        }
       }
     } else {
       // the ragged last tile, element by element
 #pragma unroll
       for (int k = 0; k < U; ++k) {
+        float w[kChunk];
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int64_t j = tbase + lane + k * kSpan + e;
+          w[e] = 0.0f;
           if (j < len) {
             float x;
             if constexpr (DT == ZERO_F16)
@@ -469,7 +607,18 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
             v[j] = vj;
             master[j] = tj;
             p16[j] = static_cast<uint16_t>(h);
+            w[e] = h2f(h);
           }
+        }
+        if constexpr (QWZ) {
+          // every lane of the wave takes part in the block maximum
+          const float scale = qwz_scale(w);
+          const uint32_t q = qwz_pack(w, scale);
+          const int64_t j0 = tbase + lane + k * kSpan;
+#pragma unroll
+          for (int e = 0; e < kChunk; ++e)
+            if (j0 + e < len) codes[j0 + e] = static_cast<uint8_t>(q >> (8 * e));
+          if (threadIdx.x == 0 && tbase + k * kSpan < len) scales[(tbase + k * kSpan) / kQwzBlock] = scale;
         }
       }
     }

@@ -32,6 +32,8 @@ constexpr int kBlocksPerCU = 8;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
 constexpr int kUpdateBlocksPerCU = 8;
 constexpr int kReduceBlocksPerCU = 6;
+// qwZ encoder and decoder: blocks (rows of one wave) per tile.
+constexpr int kQwzU = 4;
 
 thread_local char g_err[512] = "";
 
@@ -87,7 +89,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 // blocks of `kernel` on a CU (0 when the kernel's own resources already allow
 // no more than that, or when no size gives exactly `target`).  Found once per
 // device and kernel with the occupancy API and cached.
-enum CapKernel { kCapUpdateF16, kCapUpdateF32, kCapReduceStats, kCapReduce, kCapKinds };
+enum CapKernel {
+  kCapUpdateF16,
+  kCapUpdateF32,
+  kCapUpdateQwzF16,
+  kCapUpdateQwzF32,
+  kCapReduceStats,
+  kCapReduce,
+  kCapKinds
+};
 std::atomic<int> g_lds_cache[kMaxDevices][kCapKinds];
 std::atomic<bool> g_lds_init{false};
 
@@ -354,10 +364,18 @@ int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks, int64_t
   return st == ZERO_OK ? ok() : st;
 }
 
-int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
-                         float *exp_avg, float *exp_avg_sq, uint16_t *param16, int64_t len, int64_t step,
-                         const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
-                         void *ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
+
+// The update, with the qwZ encoding of its fp16 output into codes and
+// scales when qwz is set.
+int adam_step_impl(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+                   float *exp_avg, float *exp_avg_sq, uint16_t *param16, bool qwz, int8_t *codes, float *scales,
+                   int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
+                   int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "adam_step: len < 0");
   if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_F32)
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: unknown grad dtype");
@@ -375,15 +393,18 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
   if (!(std::isfinite(hp->max_grad_norm) && hp->max_grad_norm >= 0.0))
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: max_grad_norm must be finite and >= 0");
   if (len > INT64_MAX / 4) return fail(ZERO_ERR_INT_OVERFLOW, "adam_step: len too large");
+  if (qwz && len > 0 && (codes == nullptr || scales == nullptr))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: NULL qwZ codes or scales");
   if (!aligned16(grad) || !aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
-      !aligned16(param16) || !aligned16(stats))
+      !aligned16(param16) || !aligned16(stats) || !aligned16(codes) || !aligned16(scales))
     return fail(ZERO_ERR_MISALIGNED, "adam_step: device pointers must be 16-byte aligned");
   const size_t n = static_cast<size_t>(len);
   const size_t gbytes = n * (grad_dtype == ZERO_F16 ? 2 : 4);
-  const void *arr[5] = {grad, master, exp_avg, exp_avg_sq, param16};
-  const size_t sz[5] = {gbytes, n * 4, n * 4, n * 4, n * 2};
-  for (int a = 0; a < 5; ++a)
-    for (int b = a + 1; b < 5; ++b)
+  const int narr = qwz ? 7 : 5;
+  const void *arr[7] = {grad, master, exp_avg, exp_avg_sq, param16, codes, scales};
+  const size_t sz[7] = {gbytes, n * 4, n * 4, n * 4, n * 2, n, static_cast<size_t>(qwz_scales_len(len)) * 4};
+  for (int a = 0; a < narr; ++a)
+    for (int b = a + 1; b < narr; ++b)
       if (overlap(arr[a], sz[a], arr[b], sz[b])) return fail(ZERO_ERR_INVALID_ARG, "adam_step: arrays overlap");
   if (!stats_precomputed) {
     if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: workspace is NULL");
@@ -415,21 +436,113 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
   const int64_t tiles = ceil_div(len, tile);
   const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
   size_t lds = 0;
-  if (grad_dtype == ZERO_F16)
+  if (grad_dtype == ZERO_F16 && !qwz)
     st = occupancy_cap_lds(kCapUpdateF16, zs::adam_update_kernel<ZERO_F16, kUpdateU>, zs::kUpdateBlock,
                            kUpdateBlocksPerCU, &lds);
-  else
+  else if (!qwz)
     st = occupancy_cap_lds(kCapUpdateF32, zs::adam_update_kernel<ZERO_F32, kUpdateU>, zs::kUpdateBlock,
                            kUpdateBlocksPerCU, &lds);
+  else if (grad_dtype == ZERO_F16)
+    st = occupancy_cap_lds(kCapUpdateQwzF16, zs::adam_update_kernel<ZERO_F16, kUpdateU, true>, zs::kUpdateBlock,
+                           kUpdateBlocksPerCU, &lds);
+  else
+    st = occupancy_cap_lds(kCapUpdateQwzF32, zs::adam_update_kernel<ZERO_F32, kUpdateU, true>, zs::kUpdateBlock,
+                           kUpdateBlocksPerCU, &lds);
   if (st != ZERO_OK) return st;
+  uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
   clear_stale_error();
-  if (grad_dtype == ZERO_F16)
+  if (grad_dtype == ZERO_F16 && !qwz)
     zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kUpdateBlock, lds, stream>>>(
         grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
-  else
+  else if (!qwz)
     zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kUpdateBlock, lds, stream>>>(
         grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
+  else if (grad_dtype == ZERO_F16)
+    zs::adam_update_kernel<ZERO_F16, kUpdateU, true><<<grid, zs::kUpdateBlock, lds, stream>>>(
+        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, codes8, scales);
+  else
+    zs::adam_update_kernel<ZERO_F32, kUpdateU, true><<<grid, zs::kUpdateBlock, lds, stream>>>(
+        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, codes8, scales);
   st = check_launch("adam_update_kernel");
+  return st == ZERO_OK ? ok() : st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+                         float *exp_avg, float *exp_avg_sq, uint16_t *param16, int64_t len, int64_t step,
+                         const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
+                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, false, nullptr,
+                        nullptr, len, step, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+}
+
+int zero_shard_adam_step_qwz(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+                             float *exp_avg, float *exp_avg_sq, uint16_t *param16, int8_t *codes, float *scales,
+                             int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
+                             int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, true, codes, scales,
+                        len, step, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+}
+
+int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes, float *scales, hipStream_t stream) {
+  if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "qwz_quantize: len < 0");
+  if (len > INT64_MAX / 4) return fail(ZERO_ERR_INT_OVERFLOW, "qwz_quantize: len too large");
+  if (len > 0 && (x16 == nullptr || codes == nullptr || scales == nullptr))
+    return fail(ZERO_ERR_INVALID_ARG, "qwz_quantize: NULL pointer");
+  if (!aligned16(x16) || !aligned16(codes) || !aligned16(scales))
+    return fail(ZERO_ERR_MISALIGNED, "qwz_quantize: device pointers must be 16-byte aligned");
+  const size_t n = static_cast<size_t>(len), ns = static_cast<size_t>(qwz_scales_len(len)) * 4;
+  if (overlap(x16, n * 2, codes, n) || overlap(x16, n * 2, scales, ns) || overlap(codes, n, scales, ns))
+    return fail(ZERO_ERR_INVALID_ARG, "qwz_quantize: arrays overlap");
+  if (len == 0) return ok();
+  constexpr int64_t tile = static_cast<int64_t>(zs::kQwzBlock) * kQwzU;
+  const int64_t tiles = ceil_div(len, tile);
+  const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
+  clear_stale_error();
+  zs::qwz_quantize_kernel<kQwzU><<<grid, zs::kWave, 0, stream>>>(x16, len, reinterpret_cast<uint8_t *>(codes),
+                                                                 scales);
+  const int st = check_launch("qwz_quantize_kernel");
+  return st == ZERO_OK ? ok() : st;
+}
+
+int zero_qwz_allgather(const int8_t *const *codes, const float *const *scales, int32_t n_ranks, int64_t shard_len,
+                       int64_t psi, uint16_t *replica, hipStream_t stream) {
+  if (n_ranks < 1 || n_ranks > ZERO_MAX_SLICES)
+    return fail(ZERO_ERR_INVALID_ARG, "qwz_allgather: n_ranks must be in [1, %d]", ZERO_MAX_SLICES);
+  if (shard_len < 0 || shard_len % 8 != 0)
+    return fail(ZERO_ERR_INVALID_ARG, "qwz_allgather: shard_len must be a non-negative multiple of 8");
+  if (shard_len > INT64_MAX / ZERO_MAX_SLICES / 2)
+    return fail(ZERO_ERR_INT_OVERFLOW, "qwz_allgather: shard_len too large");
+  if (psi < 0 || psi > shard_len * n_ranks) return fail(ZERO_ERR_INVALID_ARG, "qwz_allgather: psi out of range");
+  if (codes == nullptr || scales == nullptr || (replica == nullptr && psi > 0))
+    return fail(ZERO_ERR_INVALID_ARG, "qwz_allgather: NULL pointer");
+  if (!aligned16(replica)) return fail(ZERO_ERR_MISALIGNED, "qwz_allgather: replica misaligned");
+  const size_t ns = static_cast<size_t>(qwz_scales_len(shard_len)) * 4;
+  zs::QwzTable tab{};
+  for (int r = 0; r < n_ranks; ++r) {
+    const int64_t first = static_cast<int64_t>(r) * shard_len;
+    const int64_t real = psi - first < shard_len ? (psi - first > 0 ? psi - first : 0) : shard_len;
+    if ((codes[r] == nullptr || scales[r] == nullptr) && real > 0)
+      return fail(ZERO_ERR_INVALID_ARG, "qwz_allgather: shard %d is NULL", r);
+    if (!aligned16(codes[r]) || !aligned16(scales[r]))
+      return fail(ZERO_ERR_MISALIGNED, "qwz_allgather: shard %d misaligned", r);
+    if (overlap(codes[r], static_cast<size_t>(shard_len), replica, static_cast<size_t>(psi) * 2) ||
+        overlap(scales[r], ns, replica, static_cast<size_t>(psi) * 2))
+      return fail(ZERO_ERR_INVALID_ARG, "qwz_allgather: replica overlaps shard %d", r);
+    tab.codes[r] = reinterpret_cast<const uint8_t *>(codes[r]);
+    tab.scales[r] = scales[r];
+  }
+  if (psi == 0 || shard_len == 0) return ok();
+  constexpr int64_t tile = static_cast<int64_t>(zs::kQwzBlock) * kQwzU;
+  const int64_t tiles = ceil_div(shard_len, tile);
+  if (tiles > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "qwz_allgather: shard_len too large");
+  clear_stale_error();
+  zs::qwz_allgather_kernel<kQwzU><<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(n_ranks)), zs::kWave, 0,
+                                    stream>>>(tab, shard_len, psi, replica);
+  const int st = check_launch("qwz_allgather_kernel");
   return st == ZERO_OK ? ok() : st;
 }
 
