@@ -407,8 +407,18 @@ __device__ __forceinline__ float wave_max(float a) {
   return a;
 }
 
-__device__ __forceinline__ uint32_t qwz_code(float x, float scale) {
-  float q = __builtin_rintf(x / scale);
+// Code of x in a block with scale > 0, given inv = 1/scale correctly
+// rounded.  The code is defined by Q = x/scale correctly rounded, then
+// rint(Q); computing Q costs a full division per value, so the quotient is
+// first estimated as t = x*inv.  |x/scale| <= 127, so |t - x/scale| and
+// |Q - x/scale| are below 2^-16 and 2^-17: whenever t lies more than 2^-13
+// from every half-integer, t and Q lie strictly on the same side of each of
+// them and rint(t) = rint(Q).  Otherwise (a possible tie) the exact quotient
+// is formed.
+__device__ __forceinline__ uint32_t qwz_code(float x, float scale, float inv) {
+  const float t = x * inv;
+  float q = __builtin_rintf(t);
+  if (!(__builtin_fabsf(t - q) < 0.5f - 0x1p-13f)) q = __builtin_rintf(x / scale);
   q = q > 127.0f ? 127.0f : q;
   q = q < -127.0f ? -127.0f : q;
   return static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xFFu;
@@ -425,9 +435,10 @@ __device__ __forceinline__ float qwz_scale(const float (&x)[kChunk]) {
 
 __device__ __forceinline__ uint32_t qwz_pack(const float (&x)[kChunk], float scale) {
   if (scale == 0.0f) return 0u;
+  const float inv = 1.0f / scale;
   uint32_t w = 0u;
 #pragma unroll
-  for (int e = 0; e < kChunk; ++e) w |= qwz_code(x[e], scale) << (8 * e);
+  for (int e = 0; e < kChunk; ++e) w |= qwz_code(x[e], scale, inv) << (8 * e);
   return w;
 }
 
@@ -435,42 +446,78 @@ __device__ __forceinline__ uint32_t qwz_decode(uint32_t code8, float scale) {
   return f2h(static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(code8))) * scale);
 }
 
-// Standalone encoder: fp16 [len] -> codes [len], scales [ceil(len/256)].
-// One wave per block, U rows (blocks) per tile, one tile per block.
+// Standalone encoder and decoder: 8 values per lane (16-byte fp16 and
+// 8-byte code accesses), so one 256-value block is a half wave and the block
+// maximum a reduction over 32 lanes.
+constexpr int kQwzLane = 8;
+constexpr int kQwzHalf = kQwzBlock / kQwzLane;  // lanes per block
+constexpr int kQwzRow = kWave * kQwzLane;       // values per wave row: 2 blocks
+static_assert(kQwzHalf == kWave / 2, "a block is half a wave");
+
+__device__ __forceinline__ float half_wave_max(float a) {
+#pragma unroll
+  for (int off = kQwzHalf / 2; off > 0; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off, kWave));
+  return a;
+}
+
+__device__ __forceinline__ float qwz_scale8(const float (&x)[kQwzLane]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kQwzLane; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(x[e]));
+  return half_wave_max(a) / 127.0f;
+}
+
+__device__ __forceinline__ u32x2 qwz_pack8(const float (&x)[kQwzLane], float scale) {
+  if (scale == 0.0f) return u32x2{0u, 0u};
+  const float inv = 1.0f / scale;
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo |= qwz_code(x[e], scale, inv) << (8 * e);
+    hi |= qwz_code(x[e + 4], scale, inv) << (8 * e);
+  }
+  return u32x2{lo, hi};
+}
+
+// fp16 [len] -> codes [len], scales [ceil(len/256)]; U rows of 2 blocks per
+// wave, one tile per block.
 template <int U>
 __global__ __launch_bounds__(kWave) void qwz_quantize_kernel(const uint16_t *__restrict__ x16, int64_t len,
                                                              uint8_t *__restrict__ codes,
                                                              float *__restrict__ scales) {
-  constexpr int64_t kTile = static_cast<int64_t>(kQwzBlock) * U;
+  constexpr int kRow = kQwzRow;
+  constexpr int64_t kTile = static_cast<int64_t>(kRow) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
-  const uint32_t lane = threadIdx.x * kChunk;
+  const uint32_t lane = threadIdx.x * kQwzLane;
+  const bool leader = (threadIdx.x & (kQwzHalf - 1)) == 0;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t tbase = tile * kTile;
     if (tbase + kTile <= len) {
-      u32x2 raw[U];
+      u32x4 raw[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) raw[k] = stream_load(reinterpret_cast<const u32x2 *>(x16 + tbase + lane + k * kQwzBlock));
+      for (int k = 0; k < U; ++k) raw[k] = stream_load(reinterpret_cast<const u32x4 *>(x16 + tbase + lane + k * kRow));
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const float x[kChunk] = {h2f(raw[k].x & 0xFFFFu), h2f(raw[k].x >> 16), h2f(raw[k].y & 0xFFFFu),
-                                 h2f(raw[k].y >> 16)};
-        const float scale = qwz_scale(x);
-        stream_store(reinterpret_cast<uint32_t *>(codes + tbase + lane + k * kQwzBlock), qwz_pack(x, scale));
-        if (threadIdx.x == 0) scales[(tbase + k * kQwzBlock) / kQwzBlock] = scale;
+        const float x[kQwzLane] = {h2f(raw[k].x & 0xFFFFu), h2f(raw[k].x >> 16), h2f(raw[k].y & 0xFFFFu),
+                                   h2f(raw[k].y >> 16),    h2f(raw[k].z & 0xFFFFu), h2f(raw[k].z >> 16),
+                                   h2f(raw[k].w & 0xFFFFu), h2f(raw[k].w >> 16)};
+        const float scale = qwz_scale8(x);
+        stream_store(reinterpret_cast<u32x2 *>(codes + tbase + lane + k * kRow), qwz_pack8(x, scale));
+        if (leader) scales[(tbase + lane + k * kRow) / kQwzBlock] = scale;
       }
     } else {
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const int64_t j0 = tbase + lane + k * kQwzBlock;
-        float x[kChunk];
+        const int64_t j0 = tbase + lane + k * kRow;
+        float x[kQwzLane];
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) x[e] = j0 + e < len ? h2f(x16[j0 + e]) : 0.0f;
-        const float scale = qwz_scale(x);
-        const uint32_t w = qwz_pack(x, scale);
+        for (int e = 0; e < kQwzLane; ++e) x[e] = j0 + e < len ? h2f(x16[j0 + e]) : 0.0f;
+        const float scale = qwz_scale8(x);
+        const u32x2 w = qwz_pack8(x, scale);
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e)
-          if (j0 + e < len) codes[j0 + e] = static_cast<uint8_t>(w >> (8 * e));
-        if (threadIdx.x == 0 && tbase + k * kQwzBlock < len) scales[(tbase + k * kQwzBlock) / kQwzBlock] = scale;
+        for (int e = 0; e < kQwzLane; ++e)
+          if (j0 + e < len) codes[j0 + e] = static_cast<uint8_t>((e < 4 ? w.x : w.y) >> (8 * (e & 3)));
+        if (leader && j0 < len) scales[j0 / kQwzBlock] = scale;
       }
     }
   }
@@ -487,7 +534,8 @@ struct QwzTable {
 template <int U>
 __global__ __launch_bounds__(kWave) void qwz_allgather_kernel(QwzTable tab, int64_t shard_len, int64_t psi,
                                                               uint16_t *__restrict__ replica) {
-  constexpr int64_t kTile = static_cast<int64_t>(kQwzBlock) * U;
+  constexpr int kRow = kQwzRow;
+  constexpr int64_t kTile = static_cast<int64_t>(kRow) * U;
   const int r = blockIdx.y;
   const int64_t first = static_cast<int64_t>(r) * shard_len;
   const int64_t real = psi - first < shard_len ? psi - first : shard_len;
@@ -496,20 +544,23 @@ __global__ __launch_bounds__(kWave) void qwz_allgather_kernel(QwzTable tab, int6
   const uint8_t *src = tab.codes[r] + tbase;
   const float *sc = tab.scales[r] + tbase / kQwzBlock;
   uint16_t *dst = replica + first + tbase;
-  const uint32_t lane = threadIdx.x * kChunk;
+  const uint32_t lane = threadIdx.x * kQwzLane;
   if (tbase + kTile <= real) {
-    uint32_t w[U];
+    u32x2 w[U];
     float scale[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      w[k] = stream_load(reinterpret_cast<const uint32_t *>(src + lane + k * kQwzBlock));
-      scale[k] = sc[k];
+      w[k] = stream_load(reinterpret_cast<const u32x2 *>(src + lane + k * kRow));
+      scale[k] = sc[(lane + k * kRow) / kQwzBlock];
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const uint32_t h0 = qwz_decode(w[k], scale[k]), h1 = qwz_decode(w[k] >> 8, scale[k]);
-      const uint32_t h2 = qwz_decode(w[k] >> 16, scale[k]), h3 = qwz_decode(w[k] >> 24, scale[k]);
-      stream_store(reinterpret_cast<u32x2 *>(dst + lane + k * kQwzBlock), u32x2{h0 | (h1 << 16), h2 | (h3 << 16)});
+      u32x4 h;
+      h.x = qwz_decode(w[k].x, scale[k]) | (qwz_decode(w[k].x >> 8, scale[k]) << 16);
+      h.y = qwz_decode(w[k].x >> 16, scale[k]) | (qwz_decode(w[k].x >> 24, scale[k]) << 16);
+      h.z = qwz_decode(w[k].y, scale[k]) | (qwz_decode(w[k].y >> 8, scale[k]) << 16);
+      h.w = qwz_decode(w[k].y >> 16, scale[k]) | (qwz_decode(w[k].y >> 24, scale[k]) << 16);
+      stream_store(reinterpret_cast<u32x4 *>(dst + lane + k * kRow), h);
     }
   } else {
     const int64_t rem = real - tbase;

@@ -32,8 +32,9 @@ constexpr int kBlocksPerCU = 8;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
 constexpr int kUpdateBlocksPerCU = 8;
 constexpr int kReduceBlocksPerCU = 6;
-// qwZ encoder and decoder: blocks (rows of one wave) per tile.
-constexpr int kQwzU = 4;
+// qwZ encoder and decoder: wave rows (512 values) per tile.
+constexpr int kQwzEncU = 4;
+constexpr int kQwzDecU = 1;
 
 thread_local char g_err[512] = "";
 
@@ -498,11 +499,11 @@ int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes, float *sc
   if (overlap(x16, n * 2, codes, n) || overlap(x16, n * 2, scales, ns) || overlap(codes, n, scales, ns))
     return fail(ZERO_ERR_INVALID_ARG, "qwz_quantize: arrays overlap");
   if (len == 0) return ok();
-  constexpr int64_t tile = static_cast<int64_t>(zs::kQwzBlock) * kQwzU;
+  constexpr int64_t tile = static_cast<int64_t>(zs::kQwzRow) * kQwzEncU;
   const int64_t tiles = ceil_div(len, tile);
   const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
   clear_stale_error();
-  zs::qwz_quantize_kernel<kQwzU><<<grid, zs::kWave, 0, stream>>>(x16, len, reinterpret_cast<uint8_t *>(codes),
+  zs::qwz_quantize_kernel<kQwzEncU><<<grid, zs::kWave, 0, stream>>>(x16, len, reinterpret_cast<uint8_t *>(codes),
                                                                  scales);
   const int st = check_launch("qwz_quantize_kernel");
   return st == ZERO_OK ? ok() : st;
@@ -536,11 +537,11 @@ int zero_qwz_allgather(const int8_t *const *codes, const float *const *scales, i
     tab.scales[r] = scales[r];
   }
   if (psi == 0 || shard_len == 0) return ok();
-  constexpr int64_t tile = static_cast<int64_t>(zs::kQwzBlock) * kQwzU;
+  constexpr int64_t tile = static_cast<int64_t>(zs::kQwzRow) * kQwzDecU;
   const int64_t tiles = ceil_div(shard_len, tile);
   if (tiles > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "qwz_allgather: shard_len too large");
   clear_stale_error();
-  zs::qwz_allgather_kernel<kQwzU><<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(n_ranks)), zs::kWave, 0,
+  zs::qwz_allgather_kernel<kQwzDecU><<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(n_ranks)), zs::kWave, 0,
                                     stream>>>(tab, shard_len, psi, replica);
   const int st = check_launch("qwz_allgather_kernel");
   return st == ZERO_OK ? ok() : st;
