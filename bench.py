@@ -43,6 +43,11 @@ REDUCE_BYTES_PER_PARAM = lambda n: 2 * n + 4   # noqa: E731
 QWZ_BYTES_PER_PARAM = 1 + 4 / 256               # int8 code + one fp32 scale per 256 values
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_update_gpt2xl_shard_counters.txt")
 REDUCE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "grad_reduce_7p5b_n64_counters.txt")
+ALLGATHER_COUNTERS_FILE = os.path.join(ROOT, "profiles", "allgather_gpt2xl_counters.txt")
+QWZ_COUNTERS_FILES = {k: os.path.join(ROOT, "profiles", f) for k, f in (
+    ("update_fused", "adam_update_qwz_gpt2xl_shard_counters.txt"),
+    ("quantize_shard", "qwz_quantize_gpt2xl_shard_counters.txt"),
+    ("allgather_gpt2xl", "qwz_allgather_gpt2xl_counters.txt"))}
 KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc", f)
                   for f in ("shard_kernels.hpp", "zero_shard.hip")]
 
@@ -153,7 +158,8 @@ def allgather_secondary(torch, zs, tk, dev, steps):
     del shards, replica
     return {"workload": "fp16 all-gather of the GPT-2-XL layout: 4 shards of 375,000,064 -> 1.5e9-value replica",
             "ms": round(sec * 1e3, 4), "params_per_s": PSI / sec, "hbm_gbps": round(gbps, 1),
-            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": 4}
+            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": 4,
+            "traffic": counter_traffic(ALLGATHER_COUNTERS_FILE)}
 
 
 def _avg_ms(torch, fn, steps):
@@ -207,17 +213,18 @@ def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, t0):
     del all_codes, all_scales, replica
     torch.cuda.empty_cache()
 
-    def entry(workload, ms, n, bytes_per):
+    def entry(key, workload, ms, n, bytes_per):
         gbps = bytes_per * n / (ms * 1e-3) / 1e9
         return {"workload": workload, "avg_launch_ms": round(ms, 4), "params_per_s": n / (ms * 1e-3),
                 "hbm_gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                "bytes_per_param": bytes_per}
+                "bytes_per_param": bytes_per, "traffic": counter_traffic(QWZ_COUNTERS_FILES[key])}
     return {
-        "update_fused": entry("GPT-2-XL shard update with qwZ encoding of the fresh fp16 weights",
+        "update_fused": entry("update_fused", "GPT-2-XL shard update with qwZ encoding of the fresh fp16 weights",
                               fused_ms, L, fused_bytes),
-        "quantize_shard": entry("qwZ encoding of the 375,000,064-value fp16 shard", enc_ms, L, enc_bytes),
-        "allgather_gpt2xl": entry("qwZ all-gather of the GPT-2-XL layout: 4 encoded shards -> 1.5e9-value "
-                                  "fp16 replica", gat_ms, PSI, gat_bytes),
+        "quantize_shard": entry("quantize_shard", "qwZ encoding of the 375,000,064-value fp16 shard", enc_ms, L,
+                                enc_bytes),
+        "allgather_gpt2xl": entry("allgather_gpt2xl", "qwZ all-gather of the GPT-2-XL layout: 4 encoded shards -> "
+                                  "1.5e9-value fp16 replica", gat_ms, PSI, gat_bytes),
     }
 
 
