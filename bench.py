@@ -19,8 +19,9 @@ around each launch, on the launch stream), a plain copy/read kernel as the
 attainable ceiling, the update with global-norm clipping, the owner-side
 reduce of 64 fp16 slices of the 7.5B / N = 64 shard (117,187,584
 parameters), the fp16 all-gather and the qwZ block-INT8 variants (encoder
-fused into the update, encoder alone, decoding all-gather), and the CPU
-oracle timed on a bounded sample of the same workload on one host core.
+fused into the update, encoder alone, decoding all-gather), the CPU oracle
+timed on a bounded sample of the same workload on one host core, and the
+multi-core SIMD host step (ZeRO-Offload's CPU Adam) on the whole shard.
 """
 from __future__ import annotations
 
@@ -262,6 +263,30 @@ def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
             "host_cpu": cpu_model, "host_threads": os.cpu_count()}
 
 
+def host_adam_secondary(torch, g, master, m, v, p16, steps=3):
+    """The multi-core SIMD host step (ZeRO-Offload's CPU Adam) on the whole
+    shard in host memory: statistics + update, all OpenMP threads."""
+    import numpy as np
+
+    from zero_partitioned_mixed_flat_amd import host_adam as ha
+    n = master.numel()
+    g_h = g.cpu().view(torch.int16).numpy().view(np.uint16).copy()
+    st = [master.cpu().numpy().copy(), m.cpu().numpy().copy(), v.cpu().numpy().copy(),
+          p16.cpu().view(torch.int16).numpy().view(np.uint16).copy()]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    isa = ha.set_isa(0)
+    ha.adam_step(g_h, *st, step=T0, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE, threads=threads)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ha.adam_step(g_h, *st, step=T0 + 1 + k, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
+                     threads=threads)
+    el = (time.perf_counter() - t0) / steps
+    return {"value": n / el, "unit": "params/s", "cores": threads, "kind": "host SIMD+OpenMP step",
+            "isa": ha.ISA_NAMES[isa], "ms_per_step": round(el * 1e3, 2),
+            "host_gbps": round((UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) * n / el / 1e9, 1),
+            "sample": f"the whole {n:,}-param shard in host memory, statistics + update, {steps} timed steps"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,9 +386,12 @@ def main():
         log(f"secondary: {secondary}")
 
     cpu = None
+    host = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(torch, g, master, m, v, p16)
         log(f"cpu baseline: {cpu}")
+        host = host_adam_secondary(torch, g, master, m, v, p16)
+        log(f"host SIMD step: {host}")
 
     rec = {
         "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
@@ -382,6 +410,7 @@ def main():
         "ceiling": ceil,
         "secondary": secondary,
         "cpu_baseline": cpu,
+        "host_adam": host,
     }
     print(json.dumps(rec), flush=True)
 

@@ -24,7 +24,9 @@ def _declared(header):
 def test_every_declared_symbol_is_exported():
     headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
     assert headers
-    libs = {"zero_shard.h": zs.library(), "zero_testkit.h": testkit.library()}
+    from zero_partitioned_mixed_flat_amd import host_adam
+    libs = {"zero_shard.h": zs.library(), "zero_testkit.h": testkit.library(),
+            "zero_host_adam.h": host_adam.library()}
     for h in headers:
         names = _declared(h)
         assert names, h
