@@ -20,11 +20,11 @@
 
 namespace {
 
-// Launch shape.  Update: U chunks of 4 elements per lane per tile, one block
-// per tile.  Stats and reduce: U chunks per lane per tile, grids capped at
-// kBlocksPerCU blocks per CU.
+// Launch shape.  Update and reduce: U chunks of 4 elements per lane per
+// tile, one block per tile.  Statistics: U 16-byte accesses per lane per
+// tile, grid capped at kBlocksPerCU blocks per CU.
 constexpr int kUpdateU = 2;
-constexpr int kStatsU = 4;
+constexpr int kStatsU = 2;
 constexpr int kReduceU = 1;
 constexpr int kReduceG = 16;
 constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
@@ -197,7 +197,8 @@ int launch_stats(const void *grad, zero_dtype_t dt, int64_t len, float s, zero_g
   int cus = 0;
   int st = cu_count(&cus);
   if (st != ZERO_OK) return st;
-  constexpr int64_t tile = static_cast<int64_t>(zs::kBlock) * zs::kChunk * kStatsU;
+  const int64_t tile = static_cast<int64_t>(zs::kBlock) * kStatsU *
+                       (dt == ZERO_F16 ? zs::stats_per_lane<ZERO_F16>() : zs::stats_per_lane<ZERO_F32>());
   const int grid = grid_for(len, tile, cus, zs::kMaxPartials);
   zs::Partial *parts = static_cast<zs::Partial *>(ws);
   clear_stale_error();
