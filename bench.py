@@ -44,6 +44,7 @@ REDUCE_BYTES_PER_PARAM = lambda n: 2 * n + 4   # noqa: E731
 QWZ_BYTES_PER_PARAM = 1 + 4 / 256               # int8 code + one fp32 scale per 256 values
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_update_gpt2xl_shard_counters.txt")
 REDUCE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "grad_reduce_7p5b_n64_counters.txt")
+STATS_COUNTERS_FILE = os.path.join(ROOT, "profiles", "grad_stats_gpt2xl_shard_counters.txt")
 ALLGATHER_COUNTERS_FILE = os.path.join(ROOT, "profiles", "allgather_gpt2xl_counters.txt")
 QWZ_COUNTERS_FILES = {k: os.path.join(ROOT, "profiles", f) for k, f in (
     ("update_fused", "adam_update_qwz_gpt2xl_shard_counters.txt"),
@@ -349,6 +350,8 @@ def main():
     dev_s = start.elapsed_time(end) * 1e-3
     upd_ms = [a.elapsed_time(b) for a, b in evs]
     upd_avg_s = sum(upd_ms) / len(upd_ms) * 1e-3
+    upd_sorted = sorted(upd_ms)
+    upd_median_ms = (upd_sorted[(len(upd_ms) - 1) // 2] + upd_sorted[len(upd_ms) // 2]) / 2
     overflow, sumsq = zs.read_stats(stats)
     log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, device {dev_s * 1e3:.3f} ms, "
         f"update avg {upd_avg_s * 1e3:.4f} ms, overflow={overflow}")
@@ -358,6 +361,10 @@ def main():
     whole_gbps = (UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) * L / step_s / 1e9
     upd_gbps = UPDATE_BYTES_PER_PARAM * L / upd_avg_s / 1e9
     traffic = counter_traffic()
+    stats_traffic = counter_traffic(STATS_COUNTERS_FILE)
+    # HBM bytes of the whole step from the counters (statistics + update; the
+    # 16-byte finalize is negligible), over the wall time of a step
+    step_counter_bytes = traffic + stats_traffic if traffic is not None and stats_traffic is not None else None
 
     secondary = None
     if not args.no_secondary:
@@ -403,9 +410,12 @@ def main():
                    "psi": PSI, "n_ranks": N_RANKS, "shard_len": L, "grad_dtype": "f16",
                    "algorithmic_bytes_per_param": UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM},
         "hbm_gbps": round(whole_gbps, 1), "hbm_frac_of_peak": round(whole_gbps / PEAK_HBM_GBPS, 4),
+        "hbm_gbps_counters": (round(step_counter_bytes / step_s / 1e9, 1) if step_counter_bytes else None),
+        "update_params_per_s": L / (upd_median_ms * 1e-3),
         "roofline": {"kernel": "adam_update_kernel<f16>", "bound": "hbm", "achieved": round(upd_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(upd_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "avg_launch_ms": round(upd_avg_s * 1e3, 4),
+                     "median_launch_ms": round(upd_median_ms, 4), "min_launch_ms": round(upd_sorted[0], 4),
                      "algorithmic_bytes_per_launch": UPDATE_BYTES_PER_PARAM * L},
         "ceiling": ceil,
         "secondary": secondary,
