@@ -65,6 +65,15 @@ int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s
 int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len,
                           hipStream_t stream_);
 
+/* Device arithmetic check: quot[j] = a[j] / b[j], root[j] = sqrt(a[j]),
+ * half[j] = binary16 of a[j] and wide[j] = binary32 of the binary16 code
+ * h[j], each with the primitive and build flags of the optimizer library
+ * (correctly rounded division and square root, round-to-nearest-even
+ * conversion, subnormals kept), for comparison with host IEEE results.  All
+ * arrays hold n elements of device memory. */
+int zero_testkit_arith_f32(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot,
+                           float *root, uint16_t *half, float *wide, hipStream_t stream_);
+
 /* Text of the HIP error behind the last -4 on the calling thread. */
 const char *zero_testkit_last_error(void);
 

@@ -380,3 +380,60 @@ def test_generator_moments(dev):
     want = 2 * student_t.sf(2.0, 3)
     p = (np.abs(t3) > 2).mean()
     assert abs(p - want) < 5 * np.sqrt(want * (1 - want) / n)
+
+
+def test_device_arithmetic_matches_host_ieee(dev):
+    """The library's primitives under its build flags: binary32 division and
+    square root correctly rounded, binary32 -> binary16 round to nearest
+    even with subnormals and overflow to inf, binary16 -> binary32 exact; on
+    2^24 random bit patterns (every class: subnormals, infinities, NaNs) plus
+    edge values, against numpy's IEEE results on the host."""
+    import torch
+    rng = np.random.default_rng(0xA417)
+    n = 1 << 24
+    a = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    b = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    edge = np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -149, 2.0 ** -126, 2.0 ** -126 - 2.0 ** -149, 3.4028235e38,
+                     np.inf, -np.inf, np.nan, 65504.0, 65519.996, 65520.0, 2.0 ** -24, 2.0 ** -25,
+                     2.0 ** -25 * (1 + 2.0 ** -23), 1.5 * 2.0 ** -24, 2.5 * 2.0 ** -24, 6.1035156e-05,
+                     6.097555e-05, 0.1, 1e-8, 0.999], dtype=np.float32)
+    m = edge.size
+    a[:m * m] = np.repeat(edge, m)
+    b[:m * m] = np.tile(edge, m)
+    # small exact-value ranges where ties and subnormals are dense
+    a[m * m:m * m + 65536] = np.arange(65536, dtype=np.float32) * np.float32(2.0 ** -25)
+    h = rng.integers(0, 2**16, n, dtype=np.uint32).astype(np.uint16)
+    h[:65536] = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    dev_a, dev_b = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    dev_h = torch.from_numpy(h.view(np.int16)).to(dev)
+    quot, root, half, wide = tk.arith_f32(dev_a, dev_b, dev_h)
+    with np.errstate(all="ignore"):
+        want = {"quot": a / b, "root": np.sqrt(a), "half": a.astype(np.float16), "wide": h.view(np.float16).astype(np.float32)}
+    got = {"quot": quot.cpu().numpy(), "root": root.cpu().numpy(),
+           "half": half.cpu().numpy().view(np.float16), "wide": wide.cpu().numpy()}
+    for name in want:
+        w, g = want[name], got[name]
+        nan_w, nan_g = np.isnan(w), np.isnan(g)
+        assert np.array_equal(nan_w, nan_g), f"{name}: NaN positions differ"
+        ui = np.uint16 if w.dtype == np.float16 else np.uint32
+        bad = np.flatnonzero((w.view(ui) != g.view(ui)) & ~nan_w)
+        assert bad.size == 0, f"{name}: {bad.size} mismatches; first at {bad[0]}: {g[bad[0]]!r} vs {w[bad[0]]!r}"
+
+
+@pytest.mark.parametrize("step", [1, 7, 1000])
+def test_zero_gradient_with_zero_moments_is_a_no_op(dev, step):
+    """g = 0 and m = v = 0: every update term is 0, so the master weights keep
+    their bits, the moments stay +0 and the fp16 copy is f16(master)."""
+    import torch
+    n = 100_003
+    master, m, v, p16 = _state(n, 77, True, dev)
+    before = _host_state(master, m, v, p16)
+    g = torch.zeros(n, dtype=torch.float16, device=dev)
+    flag, ssq = _gpu_step(g, master, m, v, p16, step=step, s=S16)
+    assert (flag, ssq) == (0, 0.0)
+    after = _host_state(master, m, v, p16)
+    assert np.array_equal(after[0].view(np.uint32), before[0].view(np.uint32))
+    assert not after[1].view(np.uint32).any() and not after[2].view(np.uint32).any()
+    ref_state, _ = _oracle_step(host_u16(g), before, step=step, s=S16)
+    assert np.array_equal(after[3], ref_state[3])
+    assert np.array_equal(after[3], before[0].astype(np.float16).view(np.uint16))

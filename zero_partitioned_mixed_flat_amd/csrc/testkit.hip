@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "shard_kernels.hpp"
 #include "zero_testkit.h"
 
 namespace {
@@ -158,6 +159,20 @@ __global__ __launch_bounds__(kBlock) void read_f32_kernel(const f32x4 *__restric
   if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < sink_len) sink[blockIdx.x] = s[0];
 }
 
+// The product's arithmetic primitives, built with the same flags as the
+// library: binary32 division and square root, the binary32 -> binary16
+// conversion of the fp16 write-back and the binary16 -> binary32 decode.
+__global__ void arith_kernel(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot, float *root,
+                             uint16_t *half, float *wide) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    quot[j] = a[j] / b[j];
+    root[j] = __builtin_sqrtf(a[j]);
+    half[j] = static_cast<uint16_t>(zs::f2h(a[j]));
+    wide[j] = zs::h2f(h[j]);
+  }
+}
+
 int cu_count() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -257,6 +272,18 @@ int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink
   const int grid = static_cast<int>(need < 1 ? 1 : (need < cap ? need : cap));
   clear_stale_error();
   read_f32_kernel<<<grid, kBlock, 0, stream_>>>(reinterpret_cast<const f32x4 *>(src), n4, sink, sink_len);
+  return launched();
+}
+
+int zero_testkit_arith_f32(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot, float *root,
+                           uint16_t *half, float *wide, hipStream_t stream_) {
+  if (n < 0) return -1;
+  if (n > 0 && (a == nullptr || b == nullptr || h == nullptr || quot == nullptr || root == nullptr ||
+                half == nullptr || wide == nullptr))
+    return -1;
+  if (n == 0) return 0;
+  clear_stale_error();
+  arith_kernel<<<grid_for(n), kBlock, 0, stream_>>>(a, b, h, n, quot, root, half, wide);
   return launched();
 }
 
