@@ -19,7 +19,8 @@ around each launch, on the launch stream), a plain copy/read kernel as the
 attainable ceiling, the update with global-norm clipping, the owner-side
 reduce of 64 fp16 slices of the 7.5B / N = 64 shard (117,187,584
 parameters), the fp16 all-gather and the qwZ block-INT8 variants (encoder
-fused into the update, encoder alone, decoding all-gather), the CPU oracle
+fused into the update, encoder alone, decoding all-gather), the step on the
+other workload shapes (tiny, 7.5B / N = 64, 7B / N = 8, 1.5e9 / N = 1), the CPU oracle
 timed on a bounded sample of the same workload on one host core, and the
 multi-core SIMD host step (ZeRO-Offload's CPU Adam) on the whole shard.
 """
@@ -230,6 +231,89 @@ def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, t0):
     }
 
 
+def _median_ms(torch, fn, steps):
+    evs = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return (ms[(len(ms) - 1) // 2] + ms[len(ms) // 2]) / 2, ms[0]
+
+
+def other_configs_secondary(torch, zs, tk, dev, steps):
+    """The step on the other workload shapes: the tiny one (reduce of 4
+    slices + update with the fp32 sum; launch-bound, cache-resident), the
+    7.5B / N = 64 shard (reduce of 64 slices + update with the fp32 sum), the
+    7B / N = 8 shard and the unpartitioned 1.5e9 model (statistics + update
+    with the fp16 gradient).  Median and minimum of `steps` timed steps."""
+    out = {}
+
+    def entry(workload, n, bytes_per, fn, t0):
+        t = [t0]
+
+        def run():
+            fn(t[0])
+            t[0] += 1
+        for _ in range(3):
+            run()
+        med, mn = _median_ms(torch, run, steps)
+        gbps = bytes_per * n / (med * 1e-3) / 1e9
+        return {"workload": workload, "shard_len": n, "median_ms": round(med, 4), "min_ms": round(mn, 4),
+                "params_per_s": n / (med * 1e-3), "bytes_per_param": bytes_per, "hbm_gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+    def reduce_step(psi, n_ranks, seed, slice_scale, s, t0, name):
+        n = zs.partition_layout(psi, n_ranks, 0, 128).shard_len
+        slices = [tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), slice_scale, seed,
+                                 tk.STREAM_GRAD + r) for r in range(n_ranks)]
+        master, m, v, p16 = tk.init_shard_state(n, seed, zero_moments=(t0 == 1), device=dev)
+        gsum = torch.empty(n, dtype=torch.float32, device=dev)
+        stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+
+        def fn(t):
+            zs.grad_reduce(slices, gsum, stats=stats, inv_grad_scale=s, workspace=ws)
+            zs.adam_step(gsum, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s,
+                         stats=stats, stats_precomputed=True)
+        res = entry(name, n, REDUCE_BYTES_PER_PARAM(n_ranks) + 30, fn, t0)
+        del slices, master, m, v, p16, gsum
+        torch.cuda.empty_cache()
+        return res
+
+    def stats_step(psi, n_ranks, seed, t0, name, student=False):
+        n = zs.partition_layout(psi, n_ranks, 0, 128).shard_len
+        master, m, v, p16 = tk.init_shard_state(n, seed, zero_moments=student, device=dev)
+        g = torch.empty(n, dtype=torch.float16, device=dev)
+        if student:
+            tk.student_t3_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD, redraw_overflow=True)
+        else:
+            tk.normal_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD)
+        stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
+
+        def fn(t):
+            zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
+            zs.adam_step(g, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
+                         stats=stats, stats_precomputed=True)
+        res = entry(name, n, UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM, fn, t0)
+        del master, m, v, p16, g
+        torch.cuda.empty_cache()
+        return res
+
+    out["tiny_n4"] = reduce_step(1_048_576, 4, 0xC1, 1e-3 * 65536, 2.0 ** -18, 1,
+                                 "tiny: psi=1,048,576, N=4, reduce of 4 slices + update (fp32 sum); "
+                                 "launch-bound and cache-resident, not a roofline figure")
+    out["7p5b_n64"] = reduce_step(7_500_000_000, 64, 0xC3, 1e-3 * 4096, 2.0 ** -18, 10,
+                                  "7.5B at N=64: reduce of 64 slices + update (fp32 sum)")
+    out["7b_n8"] = stats_step(7_000_000_000, 8, 0xC4, 1000, "7B at N=8: statistics + update (fp16 grad)")
+    out["1p5b_n1"] = stats_step(1_500_000_000, 1, 0xC5, 1,
+                                "GPT-2-XL unpartitioned (N=1): statistics + update (fp16 Student-t(3) grad, "
+                                "overflowing draws redrawn)", student=True)
+    return out
+
+
 def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
     """The oracle (single-threaded C, untuned) on the first 2^24 parameters of
     the shard: statistics then the gated update, repeated until ~10 s."""
@@ -389,7 +473,8 @@ def main():
                                         "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},
                      "qwz": qwz,
                      "reduce_n64": reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2)),
-                     "allgather_gpt2xl": allgather_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
+                     "allgather_gpt2xl": allgather_secondary(torch, zs, tk, dev, max(5, args.steps // 2)),
+                     "other_configs": other_configs_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
         log(f"secondary: {secondary}")
 
     cpu = None
