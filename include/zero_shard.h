@@ -13,13 +13,20 @@
  *
  * Conventions for every entry point:
  *   - No exceptions cross the ABI; every call returns a zero_status_t (or a
- *     size / string as documented).  On failure nothing is enqueued and
- *     zero_last_error() holds a message for the calling thread.
+ *     size / string as documented), and on failure zero_last_error() holds
+ *     a message for the calling thread.  Arguments are validated before
+ *     anything is enqueued, so a validation error enqueues nothing; a launch
+ *     failure (ZERO_ERR_HIP) may leave earlier kernels of the same call
+ *     enqueued.
  *   - Device pointers are HIP device allocations on the current device and
  *     must be 16-byte aligned (ZERO_ERR_MISALIGNED otherwise).  Every array
  *     is owned by the caller; the library never allocates or frees device
- *     memory and keeps no state between calls (a per-device CU-count cache
- *     aside).
+ *     memory and keeps no state between calls, apart from per-device caches
+ *     of the CU count and of the launch-shape LDS sizes.  Those are filled
+ *     by the first call of each kind on a device, with occupancy queries;
+ *     make that first call outside HIP graph capture.  After it, every call
+ *     enqueues kernels only (no memset, copy or allocation) and can be
+ *     captured into a graph.
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and the call returns without synchronising; outputs, including
  *     the device-resident zero_grad_stats_t, are valid once the stream has
