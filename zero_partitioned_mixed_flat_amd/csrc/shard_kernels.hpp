@@ -602,6 +602,8 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
       const float *tm = m + tbase, *tv = v + tbase, *tt0 = master + tbase;
       float x[U][kChunk];
       f32x4 mm[U], vv[U], tt[U];
+      uint32_t qq[U];  // qwZ: this lane's 4 codes of row k
+      float qs[U];     // qwZ: the scale of row k's block
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         const uint32_t j = lane + k * kSpan;
@@ -638,9 +640,40 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
         stream_store(reinterpret_cast<u32x2 *>(p16 + tbase + j), u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
         if constexpr (QWZ) {
           const float w[kChunk] = {h2f(h[0]), h2f(h[1]), h2f(h[2]), h2f(h[3])};
-          const float scale = qwz_scale(w);
-          stream_store(reinterpret_cast<uint32_t *>(codes + tbase + j), qwz_pack(w, scale));
-          if (threadIdx.x == 0) scales[(tbase + k * kSpan) / kQwzBlock] = scale;
+          qs[k] = qwz_scale(w);
+          qq[k] = qwz_pack(w, qs[k]);
+        }
+      }
+      if constexpr (QWZ) {
+        // The tile's U*256 codes are contiguous; lane l stores 4*U of them
+        // with one access: the words of lanes U*(l % (64/U)) + i of row
+        // l / (64/U), gathered with shuffles.  Measured on the 375M shard,
+        // this costs 3.8% over the plain update where one 4-byte store per
+        // row cost 7.1% (the algorithmic increase is 3.6%).
+        constexpr int kLanesPerRow = kWave / U;
+        const int l = static_cast<int>(threadIdx.x);
+        const int row = l / kLanesPerRow, src = U * (l % kLanesPerRow);
+        uint32_t word[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+          word[i] = 0u;
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            const uint32_t x = __shfl(qq[k], src + i, kWave);
+            word[i] = row == k ? x : word[i];
+          }
+        }
+        if constexpr (U == 2) {
+          stream_store(reinterpret_cast<u32x2 *>(codes + tbase + 8 * l), u32x2{word[0], word[1]});
+        } else {
+#pragma unroll
+          for (int i = 0; i < U; ++i) stream_store(reinterpret_cast<uint32_t *>(codes + tbase + 4 * (U * l + i)), word[i]);
+        }
+        if (l < U) {
+          float sc = qs[0];
+#pragma unroll
+          for (int k = 1; k < U; ++k) sc = l == k ? qs[k] : sc;
+          scales[tbase / kQwzBlock + l] = sc;
         }
       }
     } else {
