@@ -390,6 +390,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other workload shapes (profiling runs: keeps one shape per kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one rank's shard step on one GPU and supports --gpus 1 only: each "
@@ -484,8 +486,9 @@ def main():
                                         "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},
                      "qwz": qwz,
                      "reduce_n64": reduce_secondary(torch, zs, tk, dev, max(5, args.steps // 2)),
-                     "allgather_gpt2xl": allgather_secondary(torch, zs, tk, dev, max(5, args.steps // 2)),
-                     "other_configs": other_configs_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
+                     "allgather_gpt2xl": allgather_secondary(torch, zs, tk, dev, max(5, args.steps // 2))}
+        if not args.no_other_configs:
+            secondary["other_configs"] = other_configs_secondary(torch, zs, tk, dev, max(5, args.steps // 2))
         log(f"secondary: {secondary}")
 
     cpu = None
