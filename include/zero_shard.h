@@ -63,6 +63,9 @@ typedef enum {
   ZERO_ERR_INT_OVERFLOW = -5   /* a size does not fit in 64 bits */
 } zero_status_t;
 
+/* Element type of a gradient argument.  Entry points take it as int32_t, so
+ * that any value a C caller passes is well defined and rejected when it is
+ * not one of these. */
 typedef enum { ZERO_F16 = 1, ZERO_F32 = 2 } zero_dtype_t;
 
 /* One rank's shard of the flat parameter index space [0, psi). */
@@ -197,7 +200,7 @@ int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks,
  * fixed order (the result is deterministic run to run).  Errors as for the
  * reduce.
  */
-int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype,
+int zero_shard_grad_stats(const void *grad, int32_t grad_dtype,
                           int64_t len, double inv_grad_scale,
                           zero_grad_stats_t *stats, void *ws, size_t ws_bytes,
                           hipStream_t stream);
@@ -238,7 +241,7 @@ int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype,
  * -> ZERO_ERR_INVALID_ARG; misaligned
  * pointer -> ZERO_ERR_MISALIGNED; short workspace -> ZERO_ERR_WORKSPACE.
  */
-int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype,
+int zero_shard_adam_step(const void *grad, int32_t grad_dtype,
                          double inv_grad_scale, float *master, float *exp_avg,
                          float *exp_avg_sq, uint16_t *param16, int64_t len,
                          int64_t step, const zero_adam_hparams_t *hp,
@@ -264,7 +267,7 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype,
  * fp16 weight are unspecified.  codes and scales must not overlap each other
  * or the other arrays.
  */
-int zero_shard_adam_step_qwz(const void *grad, zero_dtype_t grad_dtype,
+int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype,
                              double inv_grad_scale, float *master,
                              float *exp_avg, float *exp_avg_sq,
                              uint16_t *param16, int8_t *codes, float *scales,

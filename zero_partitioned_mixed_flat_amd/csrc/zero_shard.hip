@@ -262,7 +262,7 @@ size_t zero_workspace_bytes(int64_t len) {
   return static_cast<size_t>(n) * sizeof(zs::Partial);
 }
 
-int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype, int64_t len, double inv_grad_scale,
+int zero_shard_grad_stats(const void *grad, int32_t grad_dtype, int64_t len, double inv_grad_scale,
                           zero_grad_stats_t *stats, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "grad_stats: len < 0");
   if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_F32)
@@ -274,7 +274,8 @@ int zero_shard_grad_stats(const void *grad, zero_dtype_t grad_dtype, int64_t len
   if (!aligned16(grad) || !aligned16(stats) || !aligned16(ws))
     return fail(ZERO_ERR_MISALIGNED, "grad_stats: device pointers must be 16-byte aligned");
   if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "grad_stats: workspace too small");
-  const int st = launch_stats(grad, grad_dtype, len, static_cast<float>(inv_grad_scale), stats, ws, stream);
+  const int st = launch_stats(grad, grad_dtype == ZERO_F16 ? ZERO_F16 : ZERO_F32, len,
+                              static_cast<float>(inv_grad_scale), stats, ws, stream);
   return st == ZERO_OK ? ok() : st;
 }
 
@@ -374,13 +375,14 @@ int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
 
 // The update, with the qwZ encoding of its fp16 output into codes and
 // scales when qwz is set.
-int adam_step_impl(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scale, float *master,
                    float *exp_avg, float *exp_avg_sq, uint16_t *param16, bool qwz, int8_t *codes, float *scales,
                    int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
                    int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "adam_step: len < 0");
-  if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_F32)
+  if (grad_dtype_in != ZERO_F16 && grad_dtype_in != ZERO_F32)
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: unknown grad dtype");
+  const zero_dtype_t grad_dtype = grad_dtype_in == ZERO_F16 ? ZERO_F16 : ZERO_F32;
   if (hp == nullptr || stats == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: NULL hp or stats");
   if (len > 0 && (grad == nullptr || master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr ||
                   param16 == nullptr))
@@ -473,7 +475,7 @@ int adam_step_impl(const void *grad, zero_dtype_t grad_dtype, double inv_grad_sc
 
 extern "C" {
 
-int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+int zero_shard_adam_step(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
                          float *exp_avg, float *exp_avg_sq, uint16_t *param16, int64_t len, int64_t step,
                          const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -481,7 +483,7 @@ int zero_shard_adam_step(const void *grad, zero_dtype_t grad_dtype, double inv_g
                         nullptr, len, step, hp, stats, stats_precomputed, ws, ws_bytes, stream);
 }
 
-int zero_shard_adam_step_qwz(const void *grad, zero_dtype_t grad_dtype, double inv_grad_scale, float *master,
+int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
                              float *exp_avg, float *exp_avg_sq, uint16_t *param16, int8_t *codes, float *scales,
                              int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
                              int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
