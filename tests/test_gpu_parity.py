@@ -437,3 +437,47 @@ def test_zero_gradient_with_zero_moments_is_a_no_op(dev, step):
     ref_state, _ = _oracle_step(host_u16(g), before, step=step, s=S16)
     assert np.array_equal(after[3], ref_state[3])
     assert np.array_equal(after[3], before[0].astype(np.float16).view(np.uint16))
+
+
+def test_concurrent_calls_from_two_threads_on_two_streams(dev):
+    """The library keeps no per-call state: two host threads, each with its
+    own stream and buffers, run statistics + update steps at the same time
+    and each ends with the oracle's result."""
+    import threading
+
+    import torch
+    n = 300_001
+    jobs = []
+    for i in range(2):
+        master, m, v, p16 = _state(n, 90 + i, False, dev)
+        g = _grad16(n, 90 + i, dev)
+        jobs.append(dict(state=[master, m, v, p16], g=g, before=_host_state(master, m, v, p16),
+                         g_h=host_u16(g), stream=torch.cuda.Stream(), stats=zs.new_stats(dev),
+                         ws=zs.new_workspace(n, dev), err=None))
+    torch.cuda.synchronize()
+
+    def work(job):
+        try:
+            with torch.cuda.stream(job["stream"]):
+                for t in range(1, 6):
+                    zs.grad_stats(job["g"], job["stats"], inv_grad_scale=S16, workspace=job["ws"])
+                    zs.adam_step(job["g"], *job["state"], step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16,
+                                 stats=job["stats"], stats_precomputed=True)
+            job["stream"].synchronize()
+        except Exception as e:  # reported below, on the test's thread
+            job["err"] = e
+
+    threads = [threading.Thread(target=work, args=(job,)) for job in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for i, job in enumerate(jobs):
+        assert job["err"] is None, job["err"]
+        ref = [a.copy() for a in job["before"]]
+        for t in range(1, 6):
+            rc, flag, _ = oracle.shard_adam_step(job["g_h"], *ref, step=t, lr=LR, beta1=BETAS[0], beta2=BETAS[1],
+                                                 eps=EPS, inv_scale=S16)
+            assert rc == 0 and flag == 0
+        counts = assert_state_parity(_host_state(*job["state"]), ref, f"thread {i}")
+        assert sum(counts.values()) == 0
