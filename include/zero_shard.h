@@ -129,9 +129,9 @@ int zero_model_state_bytes(double psi, int32_t n_ranks, int32_t stage,
 
 /*
  * zero_workspace_bytes -- bytes of device workspace that the statistics of a
- * shard of `len` elements need: per-block partial results, 16 bytes per 512
- * elements (about 1.6% of an fp16 gradient of that length) and never less
- * than 32 KiB.  The same buffer may be reused by consecutive calls on one stream;
+ * shard of `len` elements need: per-block partial results, 16 bytes per
+ * 1024 elements (about 0.8% of an fp16 gradient of that length) and never
+ * less than 32 KiB.  The same buffer may be reused by consecutive calls on one stream;
  * calls that share it must not run concurrently.  Returns 0 for len < 0.
  */
 size_t zero_workspace_bytes(int64_t len);

@@ -83,9 +83,9 @@ def test_model_state_bytes_matches_oracle(orc):
 def test_workspace_and_status_strings():
     assert zs.workspace_bytes(0) >= 32768 and zs.workspace_bytes(-1) == 0
     for n in (1, 10**6, 117_187_584, 10**10):
-        # 16-byte partials, one per 512 elements plus one fold level
-        assert zs.workspace_bytes(n) <= max(32768, 16 * (n // 512 + n // (512 * 4096) + 3))
-        assert zs.workspace_bytes(n) >= 16 * (n // 512)
+        # 16-byte partials, one per 1024-element reduce tile plus one fold level
+        assert zs.workspace_bytes(n) <= max(32768, 16 * (n // 1024 + n // (1024 * 4096) + 3))
+        assert zs.workspace_bytes(n) >= 16 * (n // 1024)
     lib = zs.library()
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.zero_status_string(code)

@@ -25,8 +25,8 @@ namespace {
 // tile, grid capped at kBlocksPerCU blocks per CU.
 constexpr int kUpdateU = 2;
 constexpr int kStatsU = 2;
-constexpr int kReduceU = 1;
-constexpr int kReduceG = 16;
+constexpr int kReduceU = 2;
+constexpr int kReduceG = 4;
 constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
 constexpr int kBlocksPerCU = 8;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
