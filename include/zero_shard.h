@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 3
+#define ZERO_SHARD_ABI_VERSION 4
 /* Largest number of simulated rank slices one reduce call accepts. */
 #define ZERO_MAX_SLICES 64
 /* Values per qwZ quantization block (one binary32 scale each). */
@@ -276,6 +276,37 @@ int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype,
                              zero_grad_stats_t *stats,
                              int32_t stats_precomputed, void *ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * zero_shard_adam_step_device_t -- zero_shard_adam_step (or, with codes and
+ * scales, zero_shard_adam_step_qwz) with the step number held in device
+ * memory, so that a captured HIP graph of the step can be replayed step
+ * after step with no host synchronisation: the bias corrections need t, and
+ * t must not advance over a skipped step (the overflow flag lives on the
+ * device).  Bias correction as in zero_shard_adam_step (Kingma & Ba, cited
+ * by [ZS]): bc = (float)(1 - beta^t) in double, here evaluated by the
+ * kernel.
+ *   applied_steps   device int64, the number of steps applied so far
+ *                   (0 before the first); this call uses t = *applied_steps
+ *                   + 1 and adds 1 to it when the step applies (flag 0),
+ *                   in a kernel enqueued after the update.  Must hold a
+ *                   value >= 0.
+ *   codes, scales   both NULL (no encoding) or both set (as in
+ *                   zero_shard_adam_step_qwz)
+ * Other arguments, semantics and errors as zero_shard_adam_step; a NULL
+ * counter, only one of codes/scales, or a counter overlapping another
+ * argument -> ZERO_ERR_INVALID_ARG.
+ */
+int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype,
+                                  double inv_grad_scale, float *master,
+                                  float *exp_avg, float *exp_avg_sq,
+                                  uint16_t *param16, int8_t *codes,
+                                  float *scales, int64_t len,
+                                  int64_t *applied_steps,
+                                  const zero_adam_hparams_t *hp,
+                                  zero_grad_stats_t *stats,
+                                  int32_t stats_precomputed, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /*
  * zero_qwz_quantize -- the qwZ encoder on its own ([ZS] section 5.3; [ZOS]

@@ -74,6 +74,10 @@ int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink
 int zero_testkit_arith_f32(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot,
                            float *root, uint16_t *half, float *wide, hipStream_t stream_);
 
+/* out[j] = the optimizer library's device-side bias correction
+ * (float)(1 - beta^t[j]) for n device-resident step numbers t. */
+int zero_testkit_bias_correction(double beta, const int64_t *t, int64_t n, float *out, hipStream_t stream_);
+
 /* Text of the HIP error behind the last -4 on the calling thread. */
 const char *zero_testkit_last_error(void);
 

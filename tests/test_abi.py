@@ -226,3 +226,23 @@ def test_philox_known_answers():
     for ctr, key, want in kat:
         got = testkit.philox_host(np.array([ctr], dtype=np.uint32), key)[0]
         assert tuple(int(x) for x in got) == want
+
+
+def test_adam_step_device_t_rejects_bad_arguments():
+    lib = zs.library()
+    hp = _hp()
+
+    def call(applied=8 * A, codes=None, scales=None, **kw):
+        a = dict(grad=A, dt=1, s=1.0, master=2 * A, m=3 * A, v=4 * A, p16=5 * A, n=1000, stats=6 * A, pre=1)
+        a.update(kw)
+        return lib.zero_shard_adam_step_device_t(a["grad"], a["dt"], a["s"], a["master"], a["m"], a["v"], a["p16"],
+                                                 codes, scales, a["n"], applied, ctypes.byref(hp), a["stats"],
+                                                 a["pre"], None, 0, None)
+    assert call(applied=None) == -1                      # no counter
+    assert call(applied=8 * A + 8) == -2                 # misaligned counter
+    assert call(applied=2 * A + 64) == -1                # counter inside master
+    assert call(applied=6 * A) == -1                     # counter on the statistics
+    assert call(codes=9 * A) == -1                       # codes without scales
+    assert call(scales=10 * A) == -1
+    assert call(dt=5) == -1
+    assert call(n=-1) == -1

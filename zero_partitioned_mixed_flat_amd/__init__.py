@@ -8,6 +8,7 @@ Stages 1, 2, and 3 Explained", "DeepSpeed ZeRO: Extreme Memory Efficiency"):
 * ``grad_reduce``       -- owner-side fp32 sum of N fp16 gradient slices
 * ``grad_stats``        -- overflow flag and sum of squares of the gradient
 * ``adam_step``         -- fused fp32 Adam update of master/m/v + fp16 copy
+  (``adam_step_device_t``: the same with the step number in device memory)
 * ``allgather``         -- the flat fp16 replica from the N owners' shards
 * ``qwz_quantize``, ``qwz_allgather``, ``adam_step(qwz_codes=...)`` -- the
   block-INT8 (qwZ) encoding of the fp16 shard and its decoding gather
@@ -17,12 +18,13 @@ All device work runs in the HIP library ``libzero_shard.so`` (C ABI in
 """
 from ._native import (  # noqa: F401
     STATS_BYTES, ZERO_F16, ZERO_F32, ZERO_MAX_SLICES, ZERO_QWZ_BLOCK, Layout, ZeroError, adam_step,
-    allgather, grad_reduce, grad_stats, library, model_state_bytes, new_stats, new_workspace,
+    adam_step_device_t, allgather, new_step_counter, grad_reduce, grad_stats, library, model_state_bytes, new_stats, new_workspace,
     partition_layout, qwz_allgather, qwz_quantize, qwz_scales_len, read_stats, workspace_bytes)
 
 __all__ = [
     "Layout", "ZeroError", "partition_layout", "model_state_bytes", "workspace_bytes",
     "new_workspace", "new_stats", "read_stats", "grad_reduce", "grad_stats", "adam_step", "allgather",
+    "adam_step_device_t", "new_step_counter",
     "qwz_quantize", "qwz_allgather", "qwz_scales_len",
     "library", "ZERO_F16", "ZERO_F32", "ZERO_MAX_SLICES", "ZERO_QWZ_BLOCK", "STATS_BYTES",
 ]

@@ -74,6 +74,9 @@ _lib.zero_shard_adam_step.restype = ctypes.c_int
 _lib.zero_shard_adam_step_qwz.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _p, _p, _i64, _i64,
                                           ctypes.POINTER(_HParams), _p, _i32, _p, _sz, _p]
 _lib.zero_shard_adam_step_qwz.restype = ctypes.c_int
+_lib.zero_shard_adam_step_device_t.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _p, _p, _i64, _p,
+                                               ctypes.POINTER(_HParams), _p, _i32, _p, _sz, _p]
+_lib.zero_shard_adam_step_device_t.restype = ctypes.c_int
 _lib.zero_qwz_quantize.argtypes = [_p, _i64, _p, _p, _p]
 _lib.zero_qwz_quantize.restype = ctypes.c_int
 _lib.zero_qwz_allgather.argtypes = [_p, _p, _i32, _i64, _i64, _p, _p]
@@ -253,6 +256,44 @@ def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: floa
         q = [_dev_ptr(qwz_codes, torch.int8, "qwz_codes", length),
              _dev_ptr(qwz_scales, torch.float32, "qwz_scales", qwz_scales_len(length))]
         _check(_lib.zero_shard_adam_step_qwz(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *q, *tail))
+
+
+def new_step_counter(device=None):
+    """A device int64 counter of applied steps, starting at 0."""
+    torch = _torch()
+    return torch.zeros(1, dtype=torch.int64, device=device or "cuda")
+
+
+def adam_step_device_t(grad, master, exp_avg, exp_avg_sq, param16, *, applied_steps, lr: float,
+                       betas=(0.9, 0.999), eps: float = 1e-8, inv_grad_scale: float = 1.0,
+                       max_grad_norm: float = 0.0, stats, stats_precomputed: bool = False, workspace=None,
+                       qwz_codes=None, qwz_scales=None, stream=None) -> None:
+    """adam_step with the step number in device memory: t = applied_steps + 1,
+    and applied_steps is advanced on the device only when the step applies,
+    so the call can be captured in a graph and replayed every step."""
+    torch = _torch()
+    length = master.numel()
+    g_p = _dev_ptr(grad, None, "grad", length)
+    ptrs = [_dev_ptr(master, torch.float32, "master", length),
+            _dev_ptr(exp_avg, torch.float32, "exp_avg", length),
+            _dev_ptr(exp_avg_sq, torch.float32, "exp_avg_sq", length),
+            _dev_ptr(param16, torch.float16, "param16", length)]
+    if (qwz_codes is None) != (qwz_scales is None):
+        raise ValueError("qwz_codes and qwz_scales go together")
+    q = [None, None]
+    if qwz_codes is not None:
+        q = [_dev_ptr(qwz_codes, torch.int8, "qwz_codes", length),
+             _dev_ptr(qwz_scales, torch.float32, "qwz_scales", qwz_scales_len(length))]
+    hp = _HParams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(max_grad_norm))
+    ws_p, ws_n = None, 0
+    if not stats_precomputed:
+        if workspace is None:
+            workspace = new_workspace(length, master.device)
+        ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
+    _check(_lib.zero_shard_adam_step_device_t(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *q, length,
+                                              _dev_ptr(applied_steps, torch.int64, "applied_steps", 1),
+                                              ctypes.byref(hp), _dev_ptr(stats, None, "stats"),
+                                              int(bool(stats_precomputed)), ws_p, ws_n, _stream(stream)))
 
 
 def qwz_scales_len(length: int) -> int:

@@ -63,7 +63,15 @@ __device__ __forceinline__ void stream_store(T *p, T v) {
 struct StepScalars {
   float b1, omb1, b2, omb2, bc1, bc2, lr, eps, s;
   double inv_scale, max_norm;
+  double beta1, beta2;  // for bias corrections formed on the device
 };
+
+// 1 - beta^t evaluated in double and rounded once to float: the bias
+// correction of step t (Kingma & Ba, the Adam paper the "DeepSpeed ZeRO
+// Stages" references cite).  Used when t is held in device memory.
+__device__ __forceinline__ float bias_correction(double beta, int64_t t) {
+  return static_cast<float>(1.0 - pow(beta, static_cast<double>(t)));
+}
 
 // The unscale multiplier of this step: s, or with global-norm clipping
 // active (max_norm > 0 and sqrt(sumsq) > max_norm) the double product
@@ -583,14 +591,22 @@ __global__ __launch_bounds__(kWave) void qwz_allgather_kernel(QwzTable tab, int6
 // registers.  Every block first reads the device-resident overflow flag and
 // leaves before any memory access to the states if it is set.  Launched with
 // one block (one wave) per tile of kUpdateBlock*4*U elements.
-template <zero_dtype_t DT, int U, bool QWZ = false>
+// With DEV_T the step number is t = *applied + 1, read from device memory,
+// and the two bias corrections are formed on the device from it (the host's
+// values in c are ignored); advance_step_kernel then counts the step.
+template <zero_dtype_t DT, int U, bool QWZ = false, bool DEV_T = false>
 __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     const void *__restrict__ grad, float *__restrict__ master, float *__restrict__ m,
     float *__restrict__ v, uint16_t *__restrict__ p16, int64_t len, StepScalars c,
     const zero_grad_stats_t *__restrict__ stats, uint8_t *__restrict__ codes = nullptr,
-    float *__restrict__ scales = nullptr) {
+    float *__restrict__ scales = nullptr, const int64_t *__restrict__ applied = nullptr) {
   static_assert(!QWZ || kUpdateBlock * kChunk == kQwzBlock, "one chunk row per qwZ block");
   if (stats->overflow != 0u) return;
+  if constexpr (DEV_T) {
+    const int64_t t = *applied + 1;
+    c.bc1 = bias_correction(c.beta1, t);
+    c.bc2 = bias_correction(c.beta2, t);
+  }
   const float s = step_scale(c, stats);
   constexpr int kSpan = kUpdateBlock * kChunk;  // elements of one chunk row of the block
   constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
@@ -714,6 +730,12 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
       }
     }
   }
+}
+
+// Counts an applied step: *applied += 1 unless the step was skipped.  One
+// thread; launched after the update on the same stream.
+__global__ void advance_step_kernel(const zero_grad_stats_t *__restrict__ stats, int64_t *__restrict__ applied) {
+  if (threadIdx.x == 0 && stats->overflow == 0u) *applied = *applied + 1;
 }
 
 }  // namespace zs

@@ -173,6 +173,13 @@ __global__ void arith_kernel(const float *a, const float *b, const uint16_t *h, 
   }
 }
 
+// The library's device-side bias correction 1 - beta^t for given t.
+__global__ void bias_correction_kernel(double beta, const int64_t *t, int64_t n, float *out) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    out[j] = zs::bias_correction(beta, t[j]);
+}
+
 int cu_count() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -284,6 +291,14 @@ int zero_testkit_arith_f32(const float *a, const float *b, const uint16_t *h, in
   if (n == 0) return 0;
   clear_stale_error();
   arith_kernel<<<grid_for(n), kBlock, 0, stream_>>>(a, b, h, n, quot, root, half, wide);
+  return launched();
+}
+
+int zero_testkit_bias_correction(double beta, const int64_t *t, int64_t n, float *out, hipStream_t stream_) {
+  if (n < 0 || (n > 0 && (t == nullptr || out == nullptr))) return -1;
+  if (n == 0) return 0;
+  clear_stale_error();
+  bias_correction_kernel<<<grid_for(n), kBlock, 0, stream_>>>(beta, t, n, out);
   return launched();
 }
 

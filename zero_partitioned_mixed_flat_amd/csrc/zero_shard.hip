@@ -95,6 +95,10 @@ enum CapKernel {
   kCapUpdateF32,
   kCapUpdateQwzF16,
   kCapUpdateQwzF32,
+  kCapUpdateF16T,
+  kCapUpdateF32T,
+  kCapUpdateQwzF16T,
+  kCapUpdateQwzF32T,
   kCapReduceStats,
   kCapReduce,
   kCapKinds
@@ -373,12 +377,30 @@ namespace {
 
 int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
 
+// Capped-occupancy launch of one instantiation of the update kernel.
+template <zero_dtype_t DT, bool QWZ, bool DEV_T>
+int launch_update(CapKernel cap, int grid, const void *grad, float *master, float *m, float *v, uint16_t *p16,
+                  int64_t len, const zs::StepScalars &c, const zero_grad_stats_t *stats, uint8_t *codes,
+                  float *scales, const int64_t *applied, hipStream_t stream) {
+  size_t lds = 0;
+  const int st = occupancy_cap_lds(cap, zs::adam_update_kernel<DT, kUpdateU, QWZ, DEV_T>, zs::kUpdateBlock,
+                                   kUpdateBlocksPerCU, &lds);
+  if (st != ZERO_OK) return st;
+  clear_stale_error();
+  zs::adam_update_kernel<DT, kUpdateU, QWZ, DEV_T><<<grid, zs::kUpdateBlock, lds, stream>>>(
+      grad, master, m, v, p16, len, c, stats, codes, scales, applied);
+  return check_launch("adam_update_kernel");
+}
+
 // The update, with the qwZ encoding of its fp16 output into codes and
-// scales when qwz is set.
+// scales when qwz is set, and with the step number read from (and counted
+// into) device memory when applied != NULL.
 int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scale, float *master,
                    float *exp_avg, float *exp_avg_sq, uint16_t *param16, bool qwz, int8_t *codes, float *scales,
-                   int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
-                   int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
+                   int64_t len, int64_t step, int64_t *applied, const zero_adam_hparams_t *hp,
+                   zero_grad_stats_t *stats, int32_t stats_precomputed, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  const bool dev_t = applied != nullptr;
   if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "adam_step: len < 0");
   if (grad_dtype_in != ZERO_F16 && grad_dtype_in != ZERO_F32)
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: unknown grad dtype");
@@ -387,7 +409,8 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   if (len > 0 && (grad == nullptr || master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr ||
                   param16 == nullptr))
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: NULL array");
-  if (step < 1) return fail(ZERO_ERR_INVALID_ARG, "adam_step: step must be >= 1");
+  if (!dev_t && step < 1) return fail(ZERO_ERR_INVALID_ARG, "adam_step: step must be >= 1");
+  if (!aligned16(applied)) return fail(ZERO_ERR_MISALIGNED, "adam_step: step counter misaligned");
   if (!(std::isfinite(hp->lr) && hp->lr >= 0.0)) return fail(ZERO_ERR_INVALID_ARG, "adam_step: bad lr");
   if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: betas must be in [0, 1)");
@@ -404,12 +427,16 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
     return fail(ZERO_ERR_MISALIGNED, "adam_step: device pointers must be 16-byte aligned");
   const size_t n = static_cast<size_t>(len);
   const size_t gbytes = n * (grad_dtype == ZERO_F16 ? 2 : 4);
-  const int narr = qwz ? 7 : 5;
-  const void *arr[7] = {grad, master, exp_avg, exp_avg_sq, param16, codes, scales};
-  const size_t sz[7] = {gbytes, n * 4, n * 4, n * 4, n * 2, n, static_cast<size_t>(qwz_scales_len(len)) * 4};
-  for (int a = 0; a < narr; ++a)
-    for (int b = a + 1; b < narr; ++b)
+  // the arrays, then the qwZ outputs, then the step counter, when present
+  const void *arr[8] = {grad, master, exp_avg, exp_avg_sq, param16, codes, scales, applied};
+  const size_t sz[8] = {gbytes, n * 4, n * 4, n * 4, n * 2, qwz ? n : 0,
+                        qwz ? static_cast<size_t>(qwz_scales_len(len)) * 4 : 0, dev_t ? 8u : 0u};
+  for (int a = 0; a < 8; ++a)
+    for (int b = a + 1; b < 8; ++b)
       if (overlap(arr[a], sz[a], arr[b], sz[b])) return fail(ZERO_ERR_INVALID_ARG, "adam_step: arrays overlap");
+  if (dev_t && (overlap(applied, 8, stats, sizeof(zero_grad_stats_t)) ||
+                (!stats_precomputed && overlap(applied, 8, ws, ws_bytes))))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step: step counter overlaps the statistics or the workspace");
   if (!stats_precomputed) {
     if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: workspace is NULL");
     if (!aligned16(ws)) return fail(ZERO_ERR_MISALIGNED, "adam_step: workspace misaligned");
@@ -422,8 +449,11 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   c.omb1 = static_cast<float>(1.0 - hp->beta1);
   c.b2 = static_cast<float>(hp->beta2);
   c.omb2 = static_cast<float>(1.0 - hp->beta2);
-  c.bc1 = static_cast<float>(1.0 - std::pow(hp->beta1, static_cast<double>(step)));
-  c.bc2 = static_cast<float>(1.0 - std::pow(hp->beta2, static_cast<double>(step)));
+  // with a device-resident step number the kernel forms these itself
+  c.bc1 = dev_t ? 1.0f : static_cast<float>(1.0 - std::pow(hp->beta1, static_cast<double>(step)));
+  c.bc2 = dev_t ? 1.0f : static_cast<float>(1.0 - std::pow(hp->beta2, static_cast<double>(step)));
+  c.beta1 = hp->beta1;
+  c.beta2 = hp->beta2;
   c.lr = static_cast<float>(hp->lr);
   c.eps = static_cast<float>(hp->eps);
   c.s = static_cast<float>(inv_grad_scale);
@@ -435,40 +465,33 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
     st = launch_stats(grad, grad_dtype, len, c.s, stats, ws, stream);
     if (st != ZERO_OK) return st;
   }
-  if (len == 0) return ok();
-  constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * kUpdateU;
-  const int64_t tiles = ceil_div(len, tile);
-  const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
-  size_t lds = 0;
-  if (grad_dtype == ZERO_F16 && !qwz)
-    st = occupancy_cap_lds(kCapUpdateF16, zs::adam_update_kernel<ZERO_F16, kUpdateU>, zs::kUpdateBlock,
-                           kUpdateBlocksPerCU, &lds);
-  else if (!qwz)
-    st = occupancy_cap_lds(kCapUpdateF32, zs::adam_update_kernel<ZERO_F32, kUpdateU>, zs::kUpdateBlock,
-                           kUpdateBlocksPerCU, &lds);
-  else if (grad_dtype == ZERO_F16)
-    st = occupancy_cap_lds(kCapUpdateQwzF16, zs::adam_update_kernel<ZERO_F16, kUpdateU, true>, zs::kUpdateBlock,
-                           kUpdateBlocksPerCU, &lds);
-  else
-    st = occupancy_cap_lds(kCapUpdateQwzF32, zs::adam_update_kernel<ZERO_F32, kUpdateU, true>, zs::kUpdateBlock,
-                           kUpdateBlocksPerCU, &lds);
-  if (st != ZERO_OK) return st;
-  uint8_t *codes8 = reinterpret_cast<uint8_t *>(codes);
-  clear_stale_error();
-  if (grad_dtype == ZERO_F16 && !qwz)
-    zs::adam_update_kernel<ZERO_F16, kUpdateU><<<grid, zs::kUpdateBlock, lds, stream>>>(
-        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
-  else if (!qwz)
-    zs::adam_update_kernel<ZERO_F32, kUpdateU><<<grid, zs::kUpdateBlock, lds, stream>>>(
-        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats);
-  else if (grad_dtype == ZERO_F16)
-    zs::adam_update_kernel<ZERO_F16, kUpdateU, true><<<grid, zs::kUpdateBlock, lds, stream>>>(
-        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, codes8, scales);
-  else
-    zs::adam_update_kernel<ZERO_F32, kUpdateU, true><<<grid, zs::kUpdateBlock, lds, stream>>>(
-        grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, codes8, scales);
-  st = check_launch("adam_update_kernel");
-  return st == ZERO_OK ? ok() : st;
+  if (len > 0) {
+    constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * kUpdateU;
+    const int64_t tiles = ceil_div(len, tile);
+    const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
+    uint8_t *c8 = reinterpret_cast<uint8_t *>(codes);
+    const bool f16 = grad_dtype == ZERO_F16;
+    const int key = (f16 ? 0 : 1) | (qwz ? 2 : 0) | (dev_t ? 4 : 0);
+    switch (key) {
+      case 0: st = launch_update<ZERO_F16, false, false>(kCapUpdateF16, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, nullptr, stream); break;
+      case 1: st = launch_update<ZERO_F32, false, false>(kCapUpdateF32, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, nullptr, stream); break;
+      case 2: st = launch_update<ZERO_F16, true, false>(kCapUpdateQwzF16, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, nullptr, stream); break;
+      case 3: st = launch_update<ZERO_F32, true, false>(kCapUpdateQwzF32, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, nullptr, stream); break;
+      case 4: st = launch_update<ZERO_F16, false, true>(kCapUpdateF16T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, applied, stream); break;
+      case 5: st = launch_update<ZERO_F32, false, true>(kCapUpdateF32T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, applied, stream); break;
+      case 6: st = launch_update<ZERO_F16, true, true>(kCapUpdateQwzF16T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
+      default: st = launch_update<ZERO_F32, true, true>(kCapUpdateQwzF32T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
+    }
+    if (st != ZERO_OK) return st;
+  }
+  if (dev_t) {
+    // counts the step (a skipped one is not counted), also when len == 0
+    clear_stale_error();
+    zs::advance_step_kernel<<<1, zs::kWave, 0, stream>>>(stats, applied);
+    st = check_launch("advance_step_kernel");
+    if (st != ZERO_OK) return st;
+  }
+  return ok();
 }
 
 }  // namespace
@@ -480,7 +503,7 @@ int zero_shard_adam_step(const void *grad, int32_t grad_dtype, double inv_grad_s
                          const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, false, nullptr,
-                        nullptr, len, step, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+                        nullptr, len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes, stream);
 }
 
 int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
@@ -488,7 +511,20 @@ int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_gr
                              int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
                              int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, true, codes, scales,
-                        len, step, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+                        len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+}
+
+int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
+                                  float *exp_avg, float *exp_avg_sq, uint16_t *param16, int8_t *codes,
+                                  float *scales, int64_t len, int64_t *applied_steps,
+                                  const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
+                                  int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (applied_steps == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step_device_t: NULL step counter");
+  if ((codes == nullptr) != (scales == nullptr))
+    return fail(ZERO_ERR_INVALID_ARG, "adam_step_device_t: qwZ codes and scales go together");
+  const bool qwz = codes != nullptr;
+  return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, qwz, codes, scales,
+                        len, 1, applied_steps, hp, stats, stats_precomputed, ws, ws_bytes, stream);
 }
 
 int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes, float *scales, hipStream_t stream) {

@@ -39,11 +39,12 @@ _lib.zero_testkit_inject_inf_f16.argtypes = [_p, _i64, _dbl, _u64, _u32, _p]
 _lib.zero_testkit_copy_f32.argtypes = [_p, _p, _i64, _p]
 _lib.zero_testkit_read_f32.argtypes = [_p, _i64, _p, _i32, _p]
 _lib.zero_testkit_arith_f32.argtypes = [_p, _p, _p, _i64, _p, _p, _p, _p, _p]
+_lib.zero_testkit_bias_correction.argtypes = [_dbl, _p, _i64, _p, _p]
 _lib.zero_testkit_last_error.argtypes = []
 _lib.zero_testkit_last_error.restype = ctypes.c_char_p
 for _f in ("zero_testkit_philox", "zero_testkit_normal_f32", "zero_testkit_normal_f16",
            "zero_testkit_student_t3_f16", "zero_testkit_inject_inf_f16", "zero_testkit_copy_f32",
-           "zero_testkit_read_f32", "zero_testkit_arith_f32"):
+           "zero_testkit_read_f32", "zero_testkit_arith_f32", "zero_testkit_bias_correction"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 # Philox stream ids of the workload tensors
@@ -109,6 +110,16 @@ def copy_f32(src, dst):
 def read_f32(src, sink):
     _ok(_lib.zero_testkit_read_f32(src.data_ptr(), src.numel(), sink.data_ptr(), sink.numel(), _stream()),
         "read_f32")
+
+
+def bias_correction(beta: float, t):
+    """The library's device-side (float)(1 - beta^t) for an int64 device tensor t."""
+    import torch
+    assert t.dtype == torch.int64 and t.is_contiguous()
+    out = torch.empty(t.numel(), dtype=torch.float32, device=t.device)
+    _ok(_lib.zero_testkit_bias_correction(float(beta), t.data_ptr(), t.numel(), out.data_ptr(), _stream()),
+        "bias_correction")
+    return out
 
 
 def arith_f32(a, b, h):
