@@ -33,7 +33,7 @@ constexpr int kBlocksPerCU = 8;
 constexpr int kUpdateBlocksPerCU = 8;
 constexpr int kReduceBlocksPerCU = 6;
 // qwZ encoder and decoder: wave rows (512 values) per tile.
-constexpr int kQwzEncU = 4;
+constexpr int kQwzEncU = 8;
 constexpr int kQwzDecU = 1;
 
 thread_local char g_err[512] = "";
