@@ -45,13 +45,14 @@ def test_reduce_step_gather_replay(dev):
     slices = [tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 1e-3 * 65536, 0x6A, tk.STREAM_GRAD + r)
               for r in range(N)]
     init = tk.init_shard_state(L, 0x6A, zero_moments=False, device=dev)
-    others = []
+    others, others_x = [], []
     for r in range(1, N):
         x = tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 0.02, 0x6B, tk.STREAM_MASTER + r)
         c = torch.empty(L, dtype=torch.int8, device=dev)
         s = torch.empty(zs.qwz_scales_len(L), dtype=torch.float32, device=dev)
         zs.qwz_quantize(x, c, s)
         others.append((c, s))
+        others_x.append(host_u16(x))
 
     def buffers():
         return dict(state=[t.clone() for t in init], gsum=torch.empty(L, dtype=torch.float32, device=dev),
@@ -86,7 +87,8 @@ def test_reduce_step_gather_replay(dev):
     # the oracle's sequence: reduce, statistics, clipped update, encode, decode + gather
     ref = [host_f32(init[0]), host_f32(init[1]), host_f32(init[2]), host_u16(init[3])]
     ref_sum = oracle.grad_reduce([host_u16(t) for t in slices])
-    other_dec = [oracle.qwz_dequantize(c.cpu().numpy(), s.cpu().numpy()) for c, s in others]
+    # the other ranks' shards as the oracle encodes and decodes them
+    other_dec = [oracle.qwz_dequantize(*oracle.qwz_quantize(x)) for x in others_x]
     for rep in range(4):
         graph.replay()
         run(eager)
