@@ -78,6 +78,9 @@ __device__ __forceinline__ void window_store(__amdgpu_buffer_rsrc_t w, uint32_t 
 __device__ __forceinline__ void window_store(__amdgpu_buffer_rsrc_t w, uint32_t byte_off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, w, byte_off, 0, kStreamStorePolicy);
 }
+__device__ __forceinline__ void window_store(__amdgpu_buffer_rsrc_t w, uint32_t byte_off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, w, byte_off, 0, kStreamStorePolicy);
+}
 
 // Per-step constants, each derived in double on the host and rounded once;
 // inv_scale and max_norm stay in double for the clipping factor, which
@@ -703,11 +706,14 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
             word[i] = row == k ? x : word[i];
           }
         }
-        if constexpr (U == 2) {
-          window_store(store_window(codes + tbase, kTile), 8 * l, u32x2{word[0], word[1]});
+        const auto wc = store_window(codes + tbase, kTile);
+        if constexpr (U == 1) {
+          window_store(wc, 4 * l, word[0]);
+        } else if constexpr (U == 2) {
+          window_store(wc, 8 * l, u32x2{word[0], word[1]});
         } else {
 #pragma unroll
-          for (int i = 0; i < U; ++i) stream_store(reinterpret_cast<uint32_t *>(codes + tbase + 4 * (U * l + i)), word[i]);
+          for (int i = 0; i < U; ++i) window_store(wc, 4 * (U * l + i), word[i]);
         }
         if (l < U) {
           float sc = qs[0];

@@ -23,14 +23,16 @@ namespace {
 // Launch shape.  Update and reduce: U chunks of 4 elements per lane per
 // tile, one block per tile.  Statistics: U 16-byte accesses per lane per
 // tile, grid capped at kBlocksPerCU blocks per CU.
-constexpr int kUpdateU = 2;
+constexpr int kUpdateU = 1;      // plain update
+constexpr int kUpdateQwzU = 2;   // with the qwZ encoder
 constexpr int kStatsU = 2;
 constexpr int kReduceU = 2;
 constexpr int kReduceG = 4;
 constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
 constexpr int kBlocksPerCU = 8;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
-constexpr int kUpdateBlocksPerCU = 8;
+constexpr int kUpdateBlocksPerCU = 12;
+constexpr int kUpdateQwzBlocksPerCU = 8;
 constexpr int kReduceBlocksPerCU = 6;
 // qwZ encoder and decoder: wave rows (512 values) per tile.
 constexpr int kQwzEncU = 8;
@@ -377,17 +379,25 @@ namespace {
 
 int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
 
-// Capped-occupancy launch of one instantiation of the update kernel.
+// Capped-occupancy launch of one instantiation of the update kernel, one
+// block per tile.  Measured on the 375M shard: the plain update is fastest
+// with 1 chunk per lane at 12 blocks per CU (1.546 ms; 2 chunks at 8 blocks:
+// 1.607 ms), the update with the qwZ encoder with 2 chunks at 8 blocks
+// (1.70 ms; 1 chunk at 12 blocks: 1.91 ms).
 template <zero_dtype_t DT, bool QWZ, bool DEV_T>
-int launch_update(CapKernel cap, int grid, const void *grad, float *master, float *m, float *v, uint16_t *p16,
-                  int64_t len, const zs::StepScalars &c, const zero_grad_stats_t *stats, uint8_t *codes,
-                  float *scales, const int64_t *applied, hipStream_t stream) {
+int launch_update(CapKernel cap, const void *grad, float *master, float *m, float *v, uint16_t *p16, int64_t len,
+                  const zs::StepScalars &c, const zero_grad_stats_t *stats, uint8_t *codes, float *scales,
+                  const int64_t *applied, hipStream_t stream) {
+  constexpr int U = QWZ ? kUpdateQwzU : kUpdateU;
+  constexpr int cap_blocks = QWZ ? kUpdateQwzBlocksPerCU : kUpdateBlocksPerCU;
+  constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * U;
+  const int64_t tiles = ceil_div(len, tile);
+  const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
   size_t lds = 0;
-  const int st = occupancy_cap_lds(cap, zs::adam_update_kernel<DT, kUpdateU, QWZ, DEV_T>, zs::kUpdateBlock,
-                                   kUpdateBlocksPerCU, &lds);
+  const int st = occupancy_cap_lds(cap, zs::adam_update_kernel<DT, U, QWZ, DEV_T>, zs::kUpdateBlock, cap_blocks, &lds);
   if (st != ZERO_OK) return st;
   clear_stale_error();
-  zs::adam_update_kernel<DT, kUpdateU, QWZ, DEV_T><<<grid, zs::kUpdateBlock, lds, stream>>>(
+  zs::adam_update_kernel<DT, U, QWZ, DEV_T><<<grid, zs::kUpdateBlock, lds, stream>>>(
       grad, master, m, v, p16, len, c, stats, codes, scales, applied);
   return check_launch("adam_update_kernel");
 }
@@ -466,21 +476,18 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
     if (st != ZERO_OK) return st;
   }
   if (len > 0) {
-    constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * kUpdateU;
-    const int64_t tiles = ceil_div(len, tile);
-    const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
     uint8_t *c8 = reinterpret_cast<uint8_t *>(codes);
     const bool f16 = grad_dtype == ZERO_F16;
     const int key = (f16 ? 0 : 1) | (qwz ? 2 : 0) | (dev_t ? 4 : 0);
     switch (key) {
-      case 0: st = launch_update<ZERO_F16, false, false>(kCapUpdateF16, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, nullptr, stream); break;
-      case 1: st = launch_update<ZERO_F32, false, false>(kCapUpdateF32, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, nullptr, stream); break;
-      case 2: st = launch_update<ZERO_F16, true, false>(kCapUpdateQwzF16, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, nullptr, stream); break;
-      case 3: st = launch_update<ZERO_F32, true, false>(kCapUpdateQwzF32, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, nullptr, stream); break;
-      case 4: st = launch_update<ZERO_F16, false, true>(kCapUpdateF16T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, applied, stream); break;
-      case 5: st = launch_update<ZERO_F32, false, true>(kCapUpdateF32T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, applied, stream); break;
-      case 6: st = launch_update<ZERO_F16, true, true>(kCapUpdateQwzF16T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
-      default: st = launch_update<ZERO_F32, true, true>(kCapUpdateQwzF32T, grid, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
+      case 0: st = launch_update<ZERO_F16, false, false>(kCapUpdateF16, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, nullptr, stream); break;
+      case 1: st = launch_update<ZERO_F32, false, false>(kCapUpdateF32, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, nullptr, stream); break;
+      case 2: st = launch_update<ZERO_F16, true, false>(kCapUpdateQwzF16, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, nullptr, stream); break;
+      case 3: st = launch_update<ZERO_F32, true, false>(kCapUpdateQwzF32, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, nullptr, stream); break;
+      case 4: st = launch_update<ZERO_F16, false, true>(kCapUpdateF16T, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, applied, stream); break;
+      case 5: st = launch_update<ZERO_F32, false, true>(kCapUpdateF32T, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, nullptr, nullptr, applied, stream); break;
+      case 6: st = launch_update<ZERO_F16, true, true>(kCapUpdateQwzF16T, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
+      default: st = launch_update<ZERO_F32, true, true>(kCapUpdateQwzF32T, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
     }
     if (st != ZERO_OK) return st;
   }
