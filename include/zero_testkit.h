@@ -62,6 +62,10 @@ int zero_testkit_inject_inf_f16(uint16_t *out, int64_t n, double prob, uint64_t 
  * floor(n/4)*4 floats whose per-block sums go to sink[block] for the blocks
  * below sink_len (4 B per element; at most 4 blocks per CU are launched). */
 int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream_);
+/* In place: p[j] += 1 over the first floor(n/4)*4 floats (8 B of traffic
+ * per element), with the optimizer's streaming-store policy: the attainable
+ * rate for read-modify-write streams. */
+int zero_testkit_rmw_f32(float *p, int64_t n, hipStream_t stream_);
 int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len,
                           hipStream_t stream_);
 

@@ -134,6 +134,21 @@ __global__ __launch_bounds__(kCopyBlock) void copy_f32_kernel(const f32x4 *__res
   if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 
+// In-place read-modify-write of whole 16-byte chunks (x += 1), the access
+// type of the optimizer's state streams: non-temporal loads, and stores
+// through a buffer window with the library's streaming-store policy.
+__global__ __launch_bounds__(kCopyBlock) void rmw_f32_kernel(float *__restrict__ p, int64_t n4) {
+  const int64_t base = blockIdx.x * static_cast<int64_t>(kCopyBlock);
+  if (base >= n4) return;
+  const int64_t i = base + threadIdx.x;
+  const auto w = zs::store_window(p + 4 * base, kCopyBlock * 16);
+  if (i < n4) {
+    zs::f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const zs::f32x4 *>(p) + i);
+    x += 1.0f;
+    zs::window_store(w, threadIdx.x * 16, x);
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void read_f32_kernel(const f32x4 *__restrict__ src, int64_t n4,
                                                           float *__restrict__ sink, int sink_len) {
   constexpr int U = 4;
@@ -267,6 +282,18 @@ int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s
   clear_stale_error();
   copy_f32_kernel<<<static_cast<unsigned>(blocks < 1 ? 1 : blocks), kCopyBlock, 0, stream_>>>(
       reinterpret_cast<const f32x4 *>(src), reinterpret_cast<f32x4 *>(dst), n4, src + n4 * 4, dst + n4 * 4, tail);
+  return launched();
+}
+
+int zero_testkit_rmw_f32(float *p, int64_t n, hipStream_t stream_) {
+  if (n < 0 || (n > 0 && p == nullptr)) return -1;
+  if (reinterpret_cast<uintptr_t>(p) & 15u) return -1;
+  const int64_t n4 = n / 4;
+  const int64_t blocks = (n4 + kCopyBlock - 1) / kCopyBlock;
+  if (blocks > INT32_MAX) return -1;
+  if (blocks == 0) return 0;
+  clear_stale_error();
+  rmw_f32_kernel<<<static_cast<unsigned>(blocks), kCopyBlock, 0, stream_>>>(p, n4);
   return launched();
 }
 

@@ -37,6 +37,7 @@ _lib.zero_testkit_normal_f16.argtypes = [_p, _i64, _dbl, _u64, _u32, _p]
 _lib.zero_testkit_student_t3_f16.argtypes = [_p, _i64, _dbl, _i32, _u64, _u32, _p]
 _lib.zero_testkit_inject_inf_f16.argtypes = [_p, _i64, _dbl, _u64, _u32, _p]
 _lib.zero_testkit_copy_f32.argtypes = [_p, _p, _i64, _p]
+_lib.zero_testkit_rmw_f32.argtypes = [_p, _i64, _p]
 _lib.zero_testkit_read_f32.argtypes = [_p, _i64, _p, _i32, _p]
 _lib.zero_testkit_arith_f32.argtypes = [_p, _p, _p, _i64, _p, _p, _p, _p, _p]
 _lib.zero_testkit_bias_correction.argtypes = [_dbl, _p, _i64, _p, _p]
@@ -44,7 +45,8 @@ _lib.zero_testkit_last_error.argtypes = []
 _lib.zero_testkit_last_error.restype = ctypes.c_char_p
 for _f in ("zero_testkit_philox", "zero_testkit_normal_f32", "zero_testkit_normal_f16",
            "zero_testkit_student_t3_f16", "zero_testkit_inject_inf_f16", "zero_testkit_copy_f32",
-           "zero_testkit_read_f32", "zero_testkit_arith_f32", "zero_testkit_bias_correction"):
+           "zero_testkit_read_f32", "zero_testkit_arith_f32", "zero_testkit_bias_correction",
+           "zero_testkit_rmw_f32"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 # Philox stream ids of the workload tensors
@@ -105,6 +107,10 @@ def inject_inf_f16_(t, prob: float, seed: int, stream: int = STREAM_INF):
 
 def copy_f32(src, dst):
     _ok(_lib.zero_testkit_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(), _stream()), "copy_f32")
+
+
+def rmw_f32(p):
+    _ok(_lib.zero_testkit_rmw_f32(p.data_ptr(), p.numel(), _stream()), "rmw_f32")
 
 
 def read_f32(src, sink):
