@@ -24,7 +24,7 @@ namespace {
 // tile, one block per tile.  Statistics: U 16-byte accesses per lane per
 // tile, grid capped at kBlocksPerCU blocks per CU.
 constexpr int kUpdateU = 1;      // plain update
-constexpr int kUpdateQwzU = 2;   // with the qwZ encoder
+constexpr int kUpdateQwzU = 1;   // with the qwZ encoder
 constexpr int kStatsU = 2;
 constexpr int kReduceU = 2;
 constexpr int kReduceG = 4;
@@ -32,7 +32,7 @@ constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kCh
 constexpr int kBlocksPerCU = 8;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
 constexpr int kUpdateBlocksPerCU = 12;
-constexpr int kUpdateQwzBlocksPerCU = 8;
+constexpr int kUpdateQwzBlocksPerCU = 16;
 constexpr int kReduceBlocksPerCU = 6;
 // qwZ encoder and decoder: wave rows (512 values) per tile.
 constexpr int kQwzEncU = 8;
@@ -382,8 +382,8 @@ int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
 // Capped-occupancy launch of one instantiation of the update kernel, one
 // block per tile.  Measured on the 375M shard: the plain update is fastest
 // with 1 chunk per lane at 12 blocks per CU (1.546 ms; 2 chunks at 8 blocks:
-// 1.607 ms), the update with the qwZ encoder with 2 chunks at 8 blocks
-// (1.70 ms; 1 chunk at 12 blocks: 1.91 ms).
+// 1.607 ms), the update with the qwZ encoder with 1 chunk at 16 blocks
+// (1.655 ms; 2 chunks at 8 or 10 blocks: 1.696 and 1.672 ms).
 template <zero_dtype_t DT, bool QWZ, bool DEV_T>
 int launch_update(CapKernel cap, const void *grad, float *master, float *m, float *v, uint16_t *p16, int64_t len,
                   const zs::StepScalars &c, const zero_grad_stats_t *stats, uint8_t *codes, float *scales,
