@@ -481,3 +481,25 @@ def test_concurrent_calls_from_two_threads_on_two_streams(dev):
             assert rc == 0 and flag == 0
         counts = assert_state_parity(_host_state(*job["state"]), ref, f"thread {i}")
         assert sum(counts.values()) == 0
+
+
+def test_ceiling_kernels_compute_what_they_claim(dev):
+    """The reference kernels behind the benchmark's ceiling: the copy copies,
+    the in-place read-modify-write adds 1 to every element of whole 16-byte
+    chunks and leaves a ragged tail alone, and the read sums its input."""
+    import torch
+    n = 1_000_003
+    src = tk.normal_f32_(torch.empty(n, dtype=torch.float32, device=dev), 0.0, 1.0, 0x77, tk.STREAM_MASTER)
+    dst = torch.empty_like(src)
+    tk.copy_f32(src, dst)
+    assert torch.equal(src, dst)
+    before = host_f32(dst)
+    tk.rmw_f32(dst)
+    after = host_f32(dst)
+    body = (n // 4) * 4
+    assert np.array_equal(after[:body], (before[:body] + np.float32(1.0)).astype(np.float32))
+    assert np.array_equal(after[body:], before[body:])
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    tk.read_f32(src, sink)
+    total = float(sink.double().sum())
+    assert abs(total - float(src[:body].double().sum())) <= 1e-3 * float(src[:body].abs().double().sum())
