@@ -25,11 +25,11 @@ namespace {
 // tile, grid capped at kBlocksPerCU blocks per CU.
 constexpr int kUpdateU = 1;      // plain update
 constexpr int kUpdateQwzU = 1;   // with the qwZ encoder
-constexpr int kStatsU = 2;
+constexpr int kStatsU = 4;
 constexpr int kReduceU = 2;
 constexpr int kReduceG = 4;
 constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
-constexpr int kBlocksPerCU = 8;
+constexpr int kBlocksPerCU = 4;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
 constexpr int kUpdateBlocksPerCU = 12;
 constexpr int kUpdateQwzBlocksPerCU = 16;
