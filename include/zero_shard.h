@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 4
+#define ZERO_SHARD_ABI_VERSION 5
 /* Largest number of simulated rank slices one reduce call accepts. */
 #define ZERO_MAX_SLICES 64
 /* Values per qwZ quantization block (one binary32 scale each). */
@@ -101,6 +101,16 @@ typedef struct {
   double sumsq;      /* sum over the shard of (f32(x_j) * inv_grad_scale)^2,
                         accumulated in fp64; unspecified when overflow = 1 */
 } zero_grad_stats_t;
+
+/* Device-resident step counter of zero_shard_adam_step_device_t (16 bytes,
+ * 16-byte aligned).  The caller zeroes it before the first step. */
+typedef struct {
+  int64_t applied;          /* steps applied so far; read and advanced on the
+                               device */
+  float bias_correction1;   /* written by each call: (float)(1 - beta1^t) for
+                               the t of that call */
+  float bias_correction2;   /* the same for beta2 */
+} zero_step_counter_t;
 
 /*
  * zero_partition_layout -- the disjoint, padded shard of `rank`.
@@ -286,11 +296,13 @@ int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype,
  * device).  Bias correction as in zero_shard_adam_step (Kingma & Ba, cited
  * by [ZS]): bc = (float)(1 - beta^t) in double, here evaluated by the
  * kernel.
- *   applied_steps   device int64, the number of steps applied so far
- *                   (0 before the first); this call uses t = *applied_steps
- *                   + 1 and adds 1 to it when the step applies (flag 0),
- *                   in a kernel enqueued after the update.  Must hold a
- *                   value >= 0.
+ *   applied_steps   device zero_step_counter_t; applied holds the number
+ *                   of steps applied so far (0 before the first) and must be
+ *                   >= 0.  This call uses t = applied + 1: a one-thread
+ *                   kernel enqueued before the update stores the two bias
+ *                   corrections for t into the counter (the update reads
+ *                   them from there) and adds 1 to applied when the step
+ *                   applies (flag 0).
  *   codes, scales   both NULL (no encoding) or both set (as in
  *                   zero_shard_adam_step_qwz)
  * Other arguments, semantics and errors as zero_shard_adam_step; a NULL
@@ -302,7 +314,7 @@ int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype,
                                   float *exp_avg, float *exp_avg_sq,
                                   uint16_t *param16, int8_t *codes,
                                   float *scales, int64_t len,
-                                  int64_t *applied_steps,
+                                  zero_step_counter_t *applied_steps,
                                   const zero_adam_hparams_t *hp,
                                   zero_grad_stats_t *stats,
                                   int32_t stats_precomputed, void *ws,

@@ -44,6 +44,17 @@ def _fresh_grad(g, seed):
     tk.normal_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD)
 
 
+def _assert_counter(counter, applied, t_call, where):
+    """The counter after a call numbered t_call: its count, and the two bias
+    corrections it holds, which must be the oracle's for t_call."""
+    raw = counter.cpu().numpy()
+    assert int(raw[0]) == applied, f"{where}: counted {int(raw[0])}, want {applied}"
+    bc = raw[1:2].view(np.float32)
+    st, s = oracle.adam_scalars(LR, BETAS[0], BETAS[1], EPS, 1.0, t_call)
+    assert st == 0
+    assert bc.view(np.uint32).tolist() == s[4:6].view(np.uint32).tolist(), f"{where}: bias corrections {bc}"
+
+
 @pytest.mark.parametrize("qwz", [False, True])
 def test_sequence_with_a_skipped_step(dev, qwz):
     """Six steps with fresh gradients; the third overflows, so it writes
@@ -67,13 +78,14 @@ def test_sequence_with_a_skipped_step(dev, qwz):
                               inv_grad_scale=S16, stats=stats, workspace=ws, qwz_codes=codes, qwz_scales=scales)
         got_stats = zs.read_stats(stats)
         flag = oracle.grad_stats(g_h, S16)[0]
+        t_call = t_ref + 1
         if not flag:
             t_ref += 1
         rc, rflag, rssq = oracle.shard_adam_step(g_h, *ref, step=max(t_ref, 1), lr=LR, beta1=BETAS[0],
                                                  beta2=BETAS[1], eps=EPS, inv_scale=S16)
         assert rc == 0 and rflag == flag == (1 if k == 2 else 0)
         assert_stats(got_stats, (rflag, rssq), f"step {k}")
-        assert int(applied.item()) == t_ref
+        _assert_counter(applied, t_ref, t_call, f"step {k}")
         counts = assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref, f"step {k}")
         assert sum(counts.values()) == 0
         if qwz and not flag:
@@ -108,7 +120,7 @@ def test_graph_replayed_across_steps(dev):
         zs.adam_step_device_t(g, master, m, v, p16, applied_steps=applied, lr=LR, betas=BETAS, eps=EPS,
                               inv_grad_scale=S16, stats=stats, stats_precomputed=True)
     torch.cuda.synchronize()
-    assert int(applied.item()) == 0
+    assert zs.applied_steps(applied) == 0
     t_ref = 0
     for k in range(8):
         _fresh_grad(g, 0xD80 + k)
@@ -119,12 +131,13 @@ def test_graph_replayed_across_steps(dev):
         graph.replay()
         torch.cuda.synchronize()
         flag, ssq = oracle.grad_stats(g_h, S16)
+        t_call = t_ref + 1
         t_ref += 0 if flag else 1
         assert_stats(zs.read_stats(stats), (flag, ssq), f"replay {k}")
         if not flag:
             assert oracle.adam_apply(g_h, *ref, step=t_ref, lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS,
                                      inv_scale=S16, overflow=0) == 0
-        assert int(applied.item()) == t_ref
+        _assert_counter(applied, t_ref, t_call, f"replay {k}")
         counts = assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref,
                                      f"replay {k}")
         assert sum(counts.values()) == 0

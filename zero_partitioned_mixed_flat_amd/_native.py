@@ -259,9 +259,16 @@ def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: floa
 
 
 def new_step_counter(device=None):
-    """A device int64 counter of applied steps, starting at 0."""
+    """A device zero_step_counter_t (16 bytes, held as two int64): the count
+    of applied steps, starting at 0, and the bias corrections of the last
+    call."""
     torch = _torch()
-    return torch.zeros(1, dtype=torch.int64, device=device or "cuda")
+    return torch.zeros(2, dtype=torch.int64, device=device or "cuda")
+
+
+def applied_steps(counter) -> int:
+    """The number of steps a device step counter has counted (synchronises)."""
+    return int(counter[0].item())
 
 
 def adam_step_device_t(grad, master, exp_avg, exp_avg_sq, param16, *, applied_steps, lr: float,
@@ -291,7 +298,7 @@ def adam_step_device_t(grad, master, exp_avg, exp_avg_sq, param16, *, applied_st
             workspace = new_workspace(length, master.device)
         ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
     _check(_lib.zero_shard_adam_step_device_t(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *q, length,
-                                              _dev_ptr(applied_steps, torch.int64, "applied_steps", 1),
+                                              _dev_ptr(applied_steps, torch.int64, "applied_steps", 2),
                                               ctypes.byref(hp), _dev_ptr(stats, None, "stats"),
                                               int(bool(stats_precomputed)), ws_p, ws_n, _stream(stream)))
 

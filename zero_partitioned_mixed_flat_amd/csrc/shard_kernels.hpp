@@ -89,7 +89,6 @@ __device__ __forceinline__ void window_store(__amdgpu_buffer_rsrc_t w, uint32_t 
 struct StepScalars {
   float b1, omb1, b2, omb2, bc1, bc2, lr, eps, s;
   double inv_scale, max_norm;
-  double beta1, beta2;  // for bias corrections formed on the device
 };
 
 // 1 - beta^t evaluated in double and rounded once to float: the bias
@@ -617,21 +616,20 @@ __global__ __launch_bounds__(kWave) void qwz_allgather_kernel(QwzTable tab, int6
 // registers.  Every block first reads the device-resident overflow flag and
 // leaves before any memory access to the states if it is set.  Launched with
 // one block (one wave) per tile of kUpdateBlock*4*U elements.
-// With DEV_T the step number is t = *applied + 1, read from device memory,
-// and the two bias corrections are formed on the device from it (the host's
-// values in c are ignored); advance_step_kernel then counts the step.
+// With DEV_T the two bias corrections are read from the device-resident
+// step counter, where begin_step_kernel stored them for this step (the
+// host's values in c are ignored).
 template <zero_dtype_t DT, int U, bool QWZ = false, bool DEV_T = false>
 __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     const void *__restrict__ grad, float *__restrict__ master, float *__restrict__ m,
     float *__restrict__ v, uint16_t *__restrict__ p16, int64_t len, StepScalars c,
     const zero_grad_stats_t *__restrict__ stats, uint8_t *__restrict__ codes = nullptr,
-    float *__restrict__ scales = nullptr, const int64_t *__restrict__ applied = nullptr) {
+    float *__restrict__ scales = nullptr, const zero_step_counter_t *__restrict__ counter = nullptr) {
   static_assert(!QWZ || kUpdateBlock * kChunk == kQwzBlock, "one chunk row per qwZ block");
   if (stats->overflow != 0u) return;
   if constexpr (DEV_T) {
-    const int64_t t = *applied + 1;
-    c.bc1 = bias_correction(c.beta1, t);
-    c.bc2 = bias_correction(c.beta2, t);
+    c.bc1 = counter->bias_correction1;
+    c.bc2 = counter->bias_correction2;
   }
   const float s = step_scale(c, stats);
   constexpr int kSpan = kUpdateBlock * kChunk;  // elements of one chunk row of the block
@@ -763,10 +761,19 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
   }
 }
 
-// Counts an applied step: *applied += 1 unless the step was skipped.  One
-// thread; launched after the update on the same stream.
-__global__ void advance_step_kernel(const zero_grad_stats_t *__restrict__ stats, int64_t *__restrict__ applied) {
-  if (threadIdx.x == 0 && stats->overflow == 0u) *applied = *applied + 1;
+// Opens a step numbered on the device: t = applied + 1, the two bias
+// corrections for t stored into the counter for the update to read, and the
+// step counted (applied = t) unless the statistics flag it as skipped.  One
+// thread, launched after the statistics and before the update on the same
+// stream; the update reads only the bias corrections, so counting here
+// rather than after it changes nothing.
+__global__ void begin_step_kernel(const zero_grad_stats_t *__restrict__ stats, zero_step_counter_t *__restrict__ counter,
+                                  double beta1, double beta2) {
+  if (threadIdx.x != 0) return;
+  const int64_t t = counter->applied + 1;
+  counter->bias_correction1 = bias_correction(beta1, t);
+  counter->bias_correction2 = bias_correction(beta2, t);
+  if (stats->overflow == 0u) counter->applied = t;
 }
 
 }  // namespace zs

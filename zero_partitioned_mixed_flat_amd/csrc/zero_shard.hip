@@ -387,7 +387,7 @@ int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
 template <zero_dtype_t DT, bool QWZ, bool DEV_T>
 int launch_update(CapKernel cap, const void *grad, float *master, float *m, float *v, uint16_t *p16, int64_t len,
                   const zs::StepScalars &c, const zero_grad_stats_t *stats, uint8_t *codes, float *scales,
-                  const int64_t *applied, hipStream_t stream) {
+                  const zero_step_counter_t *counter, hipStream_t stream) {
   constexpr int U = QWZ ? kUpdateQwzU : kUpdateU;
   constexpr int cap_blocks = QWZ ? kUpdateQwzBlocksPerCU : kUpdateBlocksPerCU;
   constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * U;
@@ -398,16 +398,16 @@ int launch_update(CapKernel cap, const void *grad, float *master, float *m, floa
   if (st != ZERO_OK) return st;
   clear_stale_error();
   zs::adam_update_kernel<DT, U, QWZ, DEV_T><<<grid, zs::kUpdateBlock, lds, stream>>>(
-      grad, master, m, v, p16, len, c, stats, codes, scales, applied);
+      grad, master, m, v, p16, len, c, stats, codes, scales, counter);
   return check_launch("adam_update_kernel");
 }
 
 // The update, with the qwZ encoding of its fp16 output into codes and
 // scales when qwz is set, and with the step number read from (and counted
-// into) device memory when applied != NULL.
+// into) the device-resident counter when applied != NULL.
 int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scale, float *master,
                    float *exp_avg, float *exp_avg_sq, uint16_t *param16, bool qwz, int8_t *codes, float *scales,
-                   int64_t len, int64_t step, int64_t *applied, const zero_adam_hparams_t *hp,
+                   int64_t len, int64_t step, zero_step_counter_t *applied, const zero_adam_hparams_t *hp,
                    zero_grad_stats_t *stats, int32_t stats_precomputed, void *ws, size_t ws_bytes,
                    hipStream_t stream) {
   const bool dev_t = applied != nullptr;
@@ -440,12 +440,13 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   // the arrays, then the qwZ outputs, then the step counter, when present
   const void *arr[8] = {grad, master, exp_avg, exp_avg_sq, param16, codes, scales, applied};
   const size_t sz[8] = {gbytes, n * 4, n * 4, n * 4, n * 2, qwz ? n : 0,
-                        qwz ? static_cast<size_t>(qwz_scales_len(len)) * 4 : 0, dev_t ? 8u : 0u};
+                        qwz ? static_cast<size_t>(qwz_scales_len(len)) * 4 : 0,
+                        dev_t ? sizeof(zero_step_counter_t) : 0u};
   for (int a = 0; a < 8; ++a)
     for (int b = a + 1; b < 8; ++b)
       if (overlap(arr[a], sz[a], arr[b], sz[b])) return fail(ZERO_ERR_INVALID_ARG, "adam_step: arrays overlap");
-  if (dev_t && (overlap(applied, 8, stats, sizeof(zero_grad_stats_t)) ||
-                (!stats_precomputed && overlap(applied, 8, ws, ws_bytes))))
+  if (dev_t && (overlap(applied, sizeof(zero_step_counter_t), stats, sizeof(zero_grad_stats_t)) ||
+                (!stats_precomputed && overlap(applied, sizeof(zero_step_counter_t), ws, ws_bytes))))
     return fail(ZERO_ERR_INVALID_ARG, "adam_step: step counter overlaps the statistics or the workspace");
   if (!stats_precomputed) {
     if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: workspace is NULL");
@@ -459,11 +460,9 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   c.omb1 = static_cast<float>(1.0 - hp->beta1);
   c.b2 = static_cast<float>(hp->beta2);
   c.omb2 = static_cast<float>(1.0 - hp->beta2);
-  // with a device-resident step number the kernel forms these itself
+  // with a device-resident step number begin_step_kernel forms these
   c.bc1 = dev_t ? 1.0f : static_cast<float>(1.0 - std::pow(hp->beta1, static_cast<double>(step)));
   c.bc2 = dev_t ? 1.0f : static_cast<float>(1.0 - std::pow(hp->beta2, static_cast<double>(step)));
-  c.beta1 = hp->beta1;
-  c.beta2 = hp->beta2;
   c.lr = static_cast<float>(hp->lr);
   c.eps = static_cast<float>(hp->eps);
   c.s = static_cast<float>(inv_grad_scale);
@@ -473,6 +472,14 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   int st;
   if (!stats_precomputed) {
     st = launch_stats(grad, grad_dtype, len, c.s, stats, ws, stream);
+    if (st != ZERO_OK) return st;
+  }
+  if (dev_t) {
+    // opens the step (bias corrections for t, counted unless skipped), also
+    // when len == 0
+    clear_stale_error();
+    zs::begin_step_kernel<<<1, zs::kWave, 0, stream>>>(stats, applied, hp->beta1, hp->beta2);
+    st = check_launch("begin_step_kernel");
     if (st != ZERO_OK) return st;
   }
   if (len > 0) {
@@ -489,13 +496,6 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
       case 6: st = launch_update<ZERO_F16, true, true>(kCapUpdateQwzF16T, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
       default: st = launch_update<ZERO_F32, true, true>(kCapUpdateQwzF32T, grad, master, exp_avg, exp_avg_sq, param16, len, c, stats, c8, scales, applied, stream); break;
     }
-    if (st != ZERO_OK) return st;
-  }
-  if (dev_t) {
-    // counts the step (a skipped one is not counted), also when len == 0
-    clear_stale_error();
-    zs::advance_step_kernel<<<1, zs::kWave, 0, stream>>>(stats, applied);
-    st = check_launch("advance_step_kernel");
     if (st != ZERO_OK) return st;
   }
   return ok();
@@ -523,7 +523,7 @@ int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_gr
 
 int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
                                   float *exp_avg, float *exp_avg_sq, uint16_t *param16, int8_t *codes,
-                                  float *scales, int64_t len, int64_t *applied_steps,
+                                  float *scales, int64_t len, zero_step_counter_t *applied_steps,
                                   const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
                                   int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (applied_steps == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step_device_t: NULL step counter");
