@@ -37,6 +37,12 @@ constexpr int kReduceBlocksPerCU = 6;
 // qwZ encoder and decoder: wave rows (512 values) per tile.
 constexpr int kQwzEncU = 8;
 constexpr int kQwzDecU = 1;
+// Bytes at the end of the gradient that the statistics read with the
+// default cache policy, so that the update finds them in the Infinity Cache
+// (256 MB on MI355X).  Measured on the 375M shard (fp16 gradient, 750 MB):
+// statistics + update 1.638 ms with 256 MB, 1.660 ms with none, 1.641 with
+// 192 MB, 1.638-1.640 with 288-384 MB, 1.659 with the whole gradient.
+constexpr int64_t kStatsKeepBytes = int64_t{256} << 20;
 
 thread_local char g_err[512] = "";
 
@@ -207,11 +213,13 @@ int launch_stats(const void *grad, zero_dtype_t dt, int64_t len, float s, zero_g
                        (dt == ZERO_F16 ? zs::stats_per_lane<ZERO_F16>() : zs::stats_per_lane<ZERO_F32>());
   const int grid = grid_for(len, tile, cus, zs::kMaxPartials);
   zs::Partial *parts = static_cast<zs::Partial *>(ws);
+  const int64_t keep = kStatsKeepBytes / (dt == ZERO_F16 ? 2 : 4);
+  const int64_t keep_from = len > keep ? len - keep : 0;
   clear_stale_error();
   if (dt == ZERO_F16)
-    zs::grad_stats_kernel<ZERO_F16, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts);
+    zs::grad_stats_kernel<ZERO_F16, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts, keep_from);
   else
-    zs::grad_stats_kernel<ZERO_F32, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts);
+    zs::grad_stats_kernel<ZERO_F32, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts, keep_from);
   st = check_launch("grad_stats_kernel");
   if (st != ZERO_OK) return st;
   return finalize(parts, grid, stats, stream);
