@@ -96,6 +96,18 @@ constexpr int kKeepLoadPolicy = 0;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t load_window(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRawBufferWord3);
 }
+// Stores with the policy as an immediate, for the same reason: the reduce
+// writes the bulk of its sum non-temporal and the last part, which the
+// update reads next, with sc1 alone.
+constexpr int kPlainStreamStorePolicy = 2;
+constexpr int kKeepStorePolicy = 16;
+template <int POLICY>
+__device__ __forceinline__ void window_store_as(__amdgpu_buffer_rsrc_t w, uint32_t byte_off, const float (&x)[4]) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, w, byte_off,
+      0, POLICY);
+}
+
 template <int POLICY>
 __device__ __forceinline__ u32x4 window_load(__amdgpu_buffer_rsrc_t w, uint32_t byte_off) {
   const auto r = __builtin_amdgcn_raw_buffer_load_b128(w, byte_off, 0, POLICY);
@@ -340,11 +352,14 @@ __global__ __launch_bounds__(kBlock) void fold_partials_kernel(const Partial *__
 // optionally with the statistics of (sum * s) in the same pass.  One block
 // per tile of kReduceBlock*4*U elements (one partial per block); slices are
 // read G at a time with non-temporal loads so G*U loads are in flight before
-// the in-order adds.
+// the in-order adds.  The sum is written non-temporal up to element
+// keep_from and with sc1 from there on: the update that reads the sum next
+// finds that part in the Infinity Cache.
 template <bool WITH_STATS, int U, int G>
 __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable tab, int n, int64_t len,
                                                                    float *__restrict__ out, float s,
-                                                                   Partial *__restrict__ partials) {
+                                                                   Partial *__restrict__ partials,
+                                                                   int64_t keep_from) {
 #pragma clang fp contract(off)
   constexpr int kSpan = kReduceBlock * kChunk;
   constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
@@ -391,10 +406,16 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
           }
         }
       }
+      const auto wo = store_window(out + tbase, kTile * 4);
+      if (tbase >= keep_from) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) window_store_as<kKeepStorePolicy>(wo, (lane + k * kSpan) * 4u, acc[k]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < U; ++k) window_store_as<kPlainStreamStorePolicy>(wo, (lane + k * kSpan) * 4u, acc[k]);
+      }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        stream_store(reinterpret_cast<f32x4 *>(out + tbase + lane + k * kSpan),
-                     f32x4{acc[k][0], acc[k][1], acc[k][2], acc[k][3]});
         if constexpr (WITH_STATS) {
 #pragma unroll
           for (int e = 0; e < kChunk; ++e) {
