@@ -167,11 +167,14 @@ def allgather_secondary(torch, zs, tk, dev, steps):
             "traffic": counter_traffic(ALLGATHER_COUNTERS_FILE)}
 
 
-def _avg_ms(torch, fn, steps):
-    """Mean duration of `fn`'s device work, HIP events on the current stream."""
+def _avg_ms(torch, fn, steps, before=None):
+    """Mean duration of `fn`'s device work, HIP events on the current stream;
+    `before`, when given, runs untimed ahead of each call."""
     evs = []
     for _ in range(steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if before is not None:
+            before()
         a.record()
         fn()
         b.record()
@@ -180,7 +183,7 @@ def _avg_ms(torch, fn, steps):
     return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
 
-def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, t0):
+def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, ws, t0):
     """qwZ block-INT8 weights (blocks of 256, one fp32 scale each): the update
     with the encoder fused into its write-back, the encoder alone on the fp16
     shard, and the decoding all-gather of the GPT-2-XL layout."""
@@ -194,7 +197,9 @@ def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, t0):
                      stats=stats, stats_precomputed=True, qwz_codes=codes, qwz_scales=scales)
         step[0] += 1
     fused()
-    fused_ms = _avg_ms(torch, fused, steps)
+    # each fused update follows its statistics pass, as in the step
+    fused_ms = _avg_ms(torch, fused, steps,
+                       before=lambda: zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws))
     fused_bytes = UPDATE_BYTES_PER_PARAM + QWZ_BYTES_PER_PARAM
     enc = lambda: zs.qwz_quantize(p16, codes, scales)  # noqa: E731
     enc()
@@ -469,11 +474,13 @@ def main():
     if not args.no_secondary:
         # the same update with global-norm clipping active (max norm 1; this
         # gradient's norm is about 19): the factor comes from the device sum
-        # of squares, so the kernel's traffic is unchanged
-        zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
+        # of squares, so the kernel's traffic is unchanged.  Each update
+        # follows its own statistics pass, as in the step, so that it finds
+        # the gradient's tail in the Infinity Cache like the timed update.
         clip_ms = []
         for k in range(args.steps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
             a.record()
             zs.adam_step(g, master, m, v, p16, step=T0 + 100 + k, lr=LR, betas=BETAS, eps=EPS,
                          inv_grad_scale=INV_SCALE, max_grad_norm=1.0, stats=stats, stats_precomputed=True)
@@ -482,7 +489,7 @@ def main():
         torch.cuda.synchronize()
         clip_avg = sum(a.elapsed_time(b) for a, b in clip_ms) / len(clip_ms)
         zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
-        qwz = qwz_secondary(torch, zs, tk, dev, args.steps, g, master, m, v, p16, stats, T0 + 200)
+        qwz = qwz_secondary(torch, zs, tk, dev, args.steps, g, master, m, v, p16, stats, ws, T0 + 200)
         del ws
         secondary = {"clipped_update": {"max_grad_norm": 1.0, "avg_launch_ms": round(clip_avg, 4),
                                         "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},

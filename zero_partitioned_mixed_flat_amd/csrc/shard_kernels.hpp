@@ -680,7 +680,6 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
     c.bc1 = counter->bias_correction1;
     c.bc2 = counter->bias_correction2;
   }
-  const float s = step_scale(c, stats);
   constexpr int kSpan = kUpdateBlock * kChunk;  // elements of one chunk row of the block
   constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
@@ -716,6 +715,10 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
         vv[k] = stream_load(reinterpret_cast<const f32x4 *>(tv + j));
         tt[k] = stream_load(reinterpret_cast<const f32x4 *>(tt0 + j));
       }
+      // formed after the loads are issued, so that with clipping its double
+      // square root and divide overlap their latency (measured: 1.548 ms
+      // with them ahead of the loads, 1.525 ms here, the same as unclipped)
+      const float s = step_scale(c, stats);
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         float ma[kChunk] = {mm[k].x, mm[k].y, mm[k].z, mm[k].w};
@@ -771,6 +774,7 @@ __global__ __launch_bounds__(kUpdateBlock) void adam_update_kernel(
         }
       }
     } else {
+      const float s = step_scale(c, stats);
       // the ragged last tile, element by element
 #pragma unroll
       for (int k = 0; k < U; ++k) {
