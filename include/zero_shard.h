@@ -165,7 +165,10 @@ size_t zero_workspace_bytes(int64_t len);
  *   ws, ws_bytes    device workspace of >= zero_workspace_bytes(len) bytes,
  *                   needed only when stats is not NULL
  * The sum is not averaged: a caller that wants the mean folds 1/N into
- * inv_grad_scale.  Errors: n_slices not in [1, ZERO_MAX_SLICES], len < 0,
+ * inv_grad_scale.  The last 256 MiB of out_sum are written so that they
+ * stay in the Infinity Cache: an update of the same shard enqueued right
+ * after this call reads them from there.  Errors: n_slices not in
+ * [1, ZERO_MAX_SLICES], len < 0,
  * a NULL slice/out pointer (len > 0), inv_grad_scale not finite or <= 0,
  * out_sum overlapping a slice -> ZERO_ERR_INVALID_ARG; misaligned pointer ->
  * ZERO_ERR_MISALIGNED; short workspace -> ZERO_ERR_WORKSPACE.
@@ -207,7 +210,9 @@ int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks,
  *   grad       device [len] of fp16 bit patterns (ZERO_F16) or fp32 (ZERO_F32)
  *   stats      device zero_grad_stats_t, written
  * Two kernels: per-block partials into `ws`, then one block sums them in a
- * fixed order (the result is deterministic run to run).  Errors as for the
+ * fixed order (the result is deterministic run to run).  The gradient's
+ * last 256 MiB are read so that they stay in the Infinity Cache: an update
+ * enqueued right after this call reads them from there.  Errors as for the
  * reduce.
  */
 int zero_shard_grad_stats(const void *grad, int32_t grad_dtype,
