@@ -28,7 +28,7 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wextra", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -281,8 +281,8 @@ __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restri
         } else {
           const float x[4] = {__uint_as_float(wd[0]), __uint_as_float(wd[1]), __uint_as_float(wd[2]),
                               __uint_as_float(wd[3])};
-          flag |= static_cast<uint32_t>(nonfinite_f32(x[0]) | nonfinite_f32(x[1]) | nonfinite_f32(x[2]) |
-                                        nonfinite_f32(x[3]));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) flag |= static_cast<uint32_t>(nonfinite_f32(x[q]));
           acc0 += sq_unscaled(x[0], s);
           acc1 += sq_unscaled(x[1], s);
           acc0 += sq_unscaled(x[2], s);
