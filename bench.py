@@ -427,6 +427,8 @@ def main():
     def one_step(t, ev=None):
         layout = zs.partition_layout(PSI, N_RANKS, RANK, ALIGN)          # a1 (host)
         assert layout.shard_len == L
+        if ev is not None:
+            ev[2].record()
         zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)  # a3 (2 kernels)
         if ev is not None:
             ev[0].record()
@@ -440,8 +442,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done; flag/sumsq = {zs.read_stats(stats)}")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -452,7 +453,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dev_s = start.elapsed_time(end) * 1e-3
-    upd_ms = [a.elapsed_time(b) for a, b in evs]
+    upd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    stats_ms = [e[2].elapsed_time(e[0]) for e in evs]     # statistics + finalize
+    stats_avg_s = sum(stats_ms) / len(stats_ms) * 1e-3
     upd_avg_s = sum(upd_ms) / len(upd_ms) * 1e-3
     upd_sorted = sorted(upd_ms)
     upd_median_ms = (upd_sorted[(len(upd_ms) - 1) // 2] + upd_sorted[len(upd_ms) // 2]) / 2
@@ -525,6 +528,11 @@ def main():
                      "traffic": traffic, "avg_launch_ms": round(upd_avg_s * 1e3, 4),
                      "median_launch_ms": round(upd_median_ms, 4), "min_launch_ms": round(upd_sorted[0], 4),
                      "algorithmic_bytes_per_launch": UPDATE_BYTES_PER_PARAM * L},
+        "statistics": {"kernels": "grad_stats_kernel<f16> + finalize_stats_kernel", "bound": "hbm",
+                       "avg_ms": round(stats_avg_s * 1e3, 4),
+                       "achieved": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9, 1), "unit": "GB/s",
+                       "frac": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9 / PEAK_HBM_GBPS, 4),
+                       "traffic": stats_traffic, "algorithmic_bytes_per_launch": STATS_BYTES_PER_PARAM * L},
         "ceiling": ceil,
         "secondary": secondary,
         "cpu_baseline": cpu,
