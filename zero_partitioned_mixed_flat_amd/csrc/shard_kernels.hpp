@@ -20,7 +20,7 @@
 //     memory controllers keep DRAM rows open, which measured 6-8% faster
 //     than full occupancy;
 //   * the statistics pass uses a grid-stride loop over a grid sized from the
-//     CU count (each block leaves one partial result), with 16-byte loads, 4
+//     CU count (each block leaves one partial result), with 16-byte loads, 8
 //     per lane in flight at 4 blocks per CU: non-temporal for the bulk of
 //     the gradient, cached for its last 256 MB, which the update then reads
 //     from the Infinity Cache (statistics + update 1.638 ms on the 375M
@@ -164,9 +164,25 @@ __device__ __forceinline__ bool nonfinite_f32(float x) {
 }
 
 // A packed pair of binary16 codes has an all-ones exponent in either half.
-__device__ __forceinline__ uint32_t nonfinite_f16x2(uint32_t w) {
-  return static_cast<uint32_t>((w & 0x7C00u) == 0x7C00u) |
-         static_cast<uint32_t>((w & 0x7C000000u) == 0x7C000000u);
+// The overflow test by maxima.  Without its sign bit, an fp16 bit pattern
+// is +-inf or NaN exactly when it is >= 0x7C00, and an fp32 one exactly when
+// it is >= 0x7F800000.  The streaming kernels keep the running maximum of
+// those magnitudes (two fp16 values at a time with one packed 16-bit max)
+// and compare once at the end, two instructions per pair of values instead
+// of a mask, a compare and a scalar OR per value.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 max_mag_f16x2(u16x2 m, uint32_t w) {
+  return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+}
+__device__ __forceinline__ uint32_t max_mag_f32(uint32_t m, float x) {
+  const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+  return b > m ? b : m;
+}
+__device__ __forceinline__ uint32_t nonfinite_mag_f16x2(u16x2 m) {
+  return static_cast<uint32_t>(m.x >= 0x7C00u) | static_cast<uint32_t>(m.y >= 0x7C00u);
+}
+__device__ __forceinline__ uint32_t nonfinite_mag_f32(uint32_t m) {
+  return static_cast<uint32_t>(m >= 0x7F800000u);
 }
 
 // The Adam update of one element ("DeepSpeed ZeRO Stages" 2.1 equations;
@@ -220,12 +236,15 @@ __device__ __forceinline__ void block_partial(double ssq, uint32_t flag, Partial
   }
 }
 
-// Adds (x*s)^2 in double; the product x*s is the binary32 unscaled gradient
-// the update sees, and its square is exact in double.
-__device__ __forceinline__ double sq_unscaled(float x, float s) {
+// acc + (x*s)^2 in double.  The product x*s is rounded to binary32 (the
+// unscaled gradient the update sees); its square has at most 48 significant
+// bits and lies between 2^-298 and 2^256, so it is exact in double, and one
+// fused multiply-add gives the same result as the square and the add
+// performed separately.
+__device__ __forceinline__ double add_sq_unscaled(double acc, float x, float s) {
 #pragma clang fp contract(off)
   const double d = static_cast<double>(x * s);
-  return d * d;
+  return __builtin_fma(d, d, acc);
 }
 
 // ---------------------------------------------------------------- statistics
@@ -258,6 +277,8 @@ __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restri
   const int64_t ntiles = (len + kTile - 1) / kTile;
   double acc0 = 0.0, acc1 = 0.0;
   uint32_t flag = 0u;
+  u16x2 mag16 = {0, 0};  // running maxima of the magnitudes' bit patterns
+  uint32_t mag32 = 0u;
   const uint32_t lane_bytes = threadIdx.x * 16u;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t base = tile * kTile;
@@ -274,19 +295,19 @@ __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restri
         if constexpr (DT == ZERO_F16) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            flag |= nonfinite_f16x2(wd[q]);
-            acc0 += sq_unscaled(h2f(wd[q] & 0xFFFFu), s);
-            acc1 += sq_unscaled(h2f(wd[q] >> 16), s);
+            mag16 = max_mag_f16x2(mag16, wd[q]);
+            acc0 = add_sq_unscaled(acc0, h2f(wd[q] & 0xFFFFu), s);
+            acc1 = add_sq_unscaled(acc1, h2f(wd[q] >> 16), s);
           }
         } else {
           const float x[4] = {__uint_as_float(wd[0]), __uint_as_float(wd[1]), __uint_as_float(wd[2]),
                               __uint_as_float(wd[3])};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) flag |= static_cast<uint32_t>(nonfinite_f32(x[q]));
-          acc0 += sq_unscaled(x[0], s);
-          acc1 += sq_unscaled(x[1], s);
-          acc0 += sq_unscaled(x[2], s);
-          acc1 += sq_unscaled(x[3], s);
+          for (int q = 0; q < 4; ++q) mag32 = max_mag_f32(mag32, x[q]);
+          acc0 = add_sq_unscaled(acc0, x[0], s);
+          acc1 = add_sq_unscaled(acc1, x[1], s);
+          acc0 = add_sq_unscaled(acc0, x[2], s);
+          acc1 = add_sq_unscaled(acc1, x[3], s);
         }
       }
     } else {
@@ -302,10 +323,11 @@ __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restri
           x = static_cast<const float *>(grad)[j];
           flag |= static_cast<uint32_t>(nonfinite_f32(x));
         }
-        acc0 += sq_unscaled(x, s);
+        acc0 = add_sq_unscaled(acc0, x, s);
       }
     }
   }
+  flag |= nonfinite_mag_f16x2(mag16) | nonfinite_mag_f32(mag32);
   block_partial(acc0 + acc1, flag, &partials[blockIdx.x]);
 }
 
@@ -366,6 +388,7 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
   const int64_t ntiles = (len + kTile - 1) / kTile;
   double acc0 = 0.0, acc1 = 0.0;
   uint32_t flag = 0u;
+  uint32_t mag32 = 0u;  // running maximum of the sums' magnitude bit patterns
   // addresses = a tile base that is the same for the whole block (kept in
   // scalar registers) + a 32-bit lane offset; with per-lane 64-bit addresses
   // the compiler serialises the slice loads
@@ -419,11 +442,11 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
         if constexpr (WITH_STATS) {
 #pragma unroll
           for (int e = 0; e < kChunk; ++e) {
-            flag |= static_cast<uint32_t>(nonfinite_f32(acc[k][e]));
+            mag32 = max_mag_f32(mag32, acc[k][e]);
             if (e & 1)
-              acc1 += sq_unscaled(acc[k][e], s);
+              acc1 = add_sq_unscaled(acc1, acc[k][e], s);
             else
-              acc0 += sq_unscaled(acc[k][e], s);
+              acc0 = add_sq_unscaled(acc0, acc[k][e], s);
           }
         }
       }
@@ -439,14 +462,17 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
             out[j] = a;
             if constexpr (WITH_STATS) {
               flag |= static_cast<uint32_t>(nonfinite_f32(a));
-              acc0 += sq_unscaled(a, s);
+              acc0 = add_sq_unscaled(acc0, a, s);
             }
           }
         }
       }
     }
   }
-  if constexpr (WITH_STATS) block_partial<kReduceBlock>(acc0 + acc1, flag, &partials[blockIdx.x]);
+  if constexpr (WITH_STATS) {
+    flag |= nonfinite_mag_f32(mag32);
+    block_partial<kReduceBlock>(acc0 + acc1, flag, &partials[blockIdx.x]);
+  }
 }
 
 // --------------------------------------------------------------- all-gather

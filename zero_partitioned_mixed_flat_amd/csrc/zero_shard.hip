@@ -25,7 +25,7 @@ namespace {
 // tile, grid capped at kBlocksPerCU blocks per CU.
 constexpr int kUpdateU = 1;      // plain update
 constexpr int kUpdateQwzU = 1;   // with the qwZ encoder
-constexpr int kStatsU = 4;
+constexpr int kStatsU = 8;
 constexpr int kReduceU = 2;
 constexpr int kReduceG = 4;
 constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
