@@ -56,12 +56,15 @@ def _assert_counter(counter, applied, t_call, where):
 
 
 @pytest.mark.parametrize("qwz", [False, True])
-def test_sequence_with_a_skipped_step(dev, qwz):
+@pytest.mark.parametrize("max_norm", [0.0, 0.05])
+def test_sequence_with_a_skipped_step(dev, qwz, max_norm):
     """Six steps with fresh gradients; the third overflows, so it writes
-    nothing and t goes 1, 2, (skip), 3, 4, 5; the counter ends at 5."""
+    nothing and t goes 1, 2, (skip), 3, 4, 5; the counter ends at 5.  With
+    max_norm = 0.05 every applied step is clipped (the gradient's norm is
+    about 0.3)."""
     import torch
     n = 100_003
-    say(f"device t: sequence, n={n}, qwz={qwz}")
+    say(f"device t: sequence, n={n}, qwz={qwz}, max_norm={max_norm}")
     master, m, v, p16 = tk.init_shard_state(n, 0xD7, zero_moments=True, device=dev)
     ref = [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
     g = torch.empty(n, dtype=torch.float16, device=dev)
@@ -75,14 +78,17 @@ def test_sequence_with_a_skipped_step(dev, qwz):
             g[12345] = float("inf")
         g_h = host_u16(g)
         zs.adam_step_device_t(g, master, m, v, p16, applied_steps=applied, lr=LR, betas=BETAS, eps=EPS,
-                              inv_grad_scale=S16, stats=stats, workspace=ws, qwz_codes=codes, qwz_scales=scales)
+                              inv_grad_scale=S16, max_grad_norm=max_norm, stats=stats, workspace=ws,
+                              qwz_codes=codes, qwz_scales=scales)
         got_stats = zs.read_stats(stats)
-        flag = oracle.grad_stats(g_h, S16)[0]
+        flag, ssq = oracle.grad_stats(g_h, S16)
+        if max_norm and not flag:
+            assert oracle.clip_factor(ssq, max_norm) < 1.0, "the test means every applied step to be clipped"
         t_call = t_ref + 1
         if not flag:
             t_ref += 1
         rc, rflag, rssq = oracle.shard_adam_step(g_h, *ref, step=max(t_ref, 1), lr=LR, beta1=BETAS[0],
-                                                 beta2=BETAS[1], eps=EPS, inv_scale=S16)
+                                                 beta2=BETAS[1], eps=EPS, inv_scale=S16, max_norm=max_norm)
         assert rc == 0 and rflag == flag == (1 if k == 2 else 0)
         assert_stats(got_stats, (rflag, rssq), f"step {k}")
         _assert_counter(applied, t_ref, t_call, f"step {k}")
