@@ -101,6 +101,46 @@ def test_sequence_with_a_skipped_step(dev, qwz, max_norm):
     assert t_ref == 5
 
 
+@pytest.mark.parametrize("qwz", [False, True])
+def test_fp32_gradient_sequence(dev, qwz):
+    """fp32 gradients (the reduce's output) through the device-counter step:
+    four steps, the second with a NaN, against the oracle's sequence."""
+    import torch
+    n = 70_001
+    say(f"device t: fp32 gradient sequence, n={n}, qwz={qwz}")
+    master, m, v, p16 = tk.init_shard_state(n, 0xD9, zero_moments=True, device=dev)
+    ref = [host_f32(master), host_f32(m), host_f32(v), host_u16(p16)]
+    g = torch.empty(n, dtype=torch.float32, device=dev)
+    stats, ws, applied = zs.new_stats(dev), zs.new_workspace(n, dev), zs.new_step_counter(dev)
+    codes = torch.empty(n, dtype=torch.int8, device=dev) if qwz else None
+    scales = torch.empty(zs.qwz_scales_len(n), dtype=torch.float32, device=dev) if qwz else None
+    s = 2.0 ** -18
+    t_ref = 0
+    for k in range(4):
+        tk.normal_f32_(g, 0.0, 1e-3 / s, 0xD90 + k, tk.STREAM_GRAD)
+        if k == 1:
+            g[n // 2] = float("nan")
+        g_h = host_f32(g)
+        zs.adam_step_device_t(g, master, m, v, p16, applied_steps=applied, lr=LR, betas=BETAS, eps=EPS,
+                              inv_grad_scale=s, stats=stats, workspace=ws, qwz_codes=codes, qwz_scales=scales)
+        flag = oracle.grad_stats(g_h, s)[0]
+        t_call = t_ref + 1
+        t_ref += 0 if flag else 1
+        rc, rflag, rssq = oracle.shard_adam_step(g_h, *ref, step=t_call, lr=LR, beta1=BETAS[0], beta2=BETAS[1],
+                                                 eps=EPS, inv_scale=s)
+        assert rc == 0 and rflag == flag == (1 if k == 1 else 0)
+        assert_stats(zs.read_stats(stats), (rflag, rssq), f"fp32 step {k}")
+        _assert_counter(applied, t_ref, t_call, f"fp32 step {k}")
+        counts = assert_state_parity([host_f32(master), host_f32(m), host_f32(v), host_u16(p16)], ref,
+                                     f"fp32 step {k}")
+        assert sum(counts.values()) == 0
+        if qwz and not flag:
+            rc_codes, rc_scales = oracle.qwz_quantize(ref[3])
+            assert np.array_equal(codes.cpu().numpy(), rc_codes)
+            assert np.array_equal(scales.cpu().numpy().view(np.uint32), rc_scales.view(np.uint32))
+    assert t_ref == 3
+
+
 def test_graph_replayed_across_steps(dev):
     """Statistics + the device-t update captured once; before each replay
     the gradient buffer is refilled in place (eagerly) with the next step's
