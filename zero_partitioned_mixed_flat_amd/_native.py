@@ -266,7 +266,7 @@ def new_step_counter(device=None):
     return torch.zeros(2, dtype=torch.int64, device=device or "cuda")
 
 
-def applied_steps(counter) -> int:
+def read_step_counter(counter) -> int:
     """The number of steps a device step counter has counted (synchronises)."""
     return int(counter[0].item())
 
