@@ -361,6 +361,11 @@ int zero_qwz_allgather(const int8_t *const *codes,
                        int64_t shard_len, int64_t psi, uint16_t *replica,
                        hipStream_t stream);
 
+/* ZERO_SHARD_ABI_VERSION as the library was built, so that a binding can
+ * refuse a library built from another version of this header.  Host only;
+ * no error. */
+int zero_shard_abi_version(void);
+
 /* Static text for a status code. */
 const char *zero_status_string(int status);
 

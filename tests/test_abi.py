@@ -40,7 +40,16 @@ def test_shard_header_declares_the_path():
     assert {"zero_partition_layout", "zero_model_state_bytes", "zero_workspace_bytes",
             "zero_shard_grad_reduce", "zero_shard_grad_stats", "zero_shard_adam_step",
             "zero_shard_allgather", "zero_shard_adam_step_qwz", "zero_qwz_quantize", "zero_qwz_allgather",
-            "zero_status_string", "zero_last_error"} <= names
+            "zero_shard_adam_step_device_t", "zero_status_string", "zero_last_error",
+            "zero_shard_abi_version"} <= names
+
+
+def test_abi_version_matches_header():
+    text = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
+    version = int(re.search(r"#define ZERO_SHARD_ABI_VERSION (\d+)", text).group(1))
+    assert zs.library().zero_shard_abi_version() == version
+    from zero_partitioned_mixed_flat_amd import _native
+    assert _native.ZERO_SHARD_ABI_VERSION == version
 
 
 def test_layout_matches_oracle(orc):

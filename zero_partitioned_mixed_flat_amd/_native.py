@@ -19,7 +19,7 @@ LIB_PATH = _build.library_path("libzero_shard.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m zero_partitioned_mixed_flat_amd.build)")
+        "(python zero_partitioned_mixed_flat_amd/build.py)")
 
 # PyTorch ships its own HIP runtime (SONAME libamdhip64.so.7).  Loading torch
 # first makes this library bind to that same runtime; loading it first would
@@ -27,6 +27,15 @@ if not os.path.exists(LIB_PATH):
 import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+# the version of include/zero_shard.h this binding is written against
+ZERO_SHARD_ABI_VERSION = 5
+_lib.zero_shard_abi_version.argtypes = []
+_lib.zero_shard_abi_version.restype = ctypes.c_int
+if _lib.zero_shard_abi_version() != ZERO_SHARD_ABI_VERSION:
+    raise ImportError(
+        f"{LIB_PATH} implements ABI version {_lib.zero_shard_abi_version()}, this binding needs "
+        f"{ZERO_SHARD_ABI_VERSION}: rebuild it (python zero_partitioned_mixed_flat_amd/build.py)")
 
 ZERO_OK = 0
 ZERO_ERR_INVALID_ARG = -1

@@ -622,4 +622,6 @@ const char *zero_status_string(int status) {
 
 const char *zero_last_error(void) { return g_err; }
 
+int zero_shard_abi_version(void) { return ZERO_SHARD_ABI_VERSION; }
+
 }  // extern "C"

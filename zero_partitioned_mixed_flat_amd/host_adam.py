@@ -13,7 +13,7 @@ from . import build as _build
 LIB_PATH = _build.library_path("libzero_host_adam.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the libraries first "
-                      "(python -m zero_partitioned_mixed_flat_amd.build)")
+                      "(python zero_partitioned_mixed_flat_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

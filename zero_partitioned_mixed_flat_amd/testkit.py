@@ -21,7 +21,7 @@ from . import build as _build
 
 LIB_PATH = _build.library_path("libzero_testkit.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it (python -m zero_partitioned_mixed_flat_amd.build)")
+    raise ImportError(f"{LIB_PATH} is missing: build it (python zero_partitioned_mixed_flat_amd/build.py)")
 
 # PyTorch ships its own HIP runtime (SONAME libamdhip64.so.7).  Loading torch
 # first makes this library bind to that same runtime; loading it first would
