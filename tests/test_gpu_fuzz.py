@@ -121,3 +121,42 @@ def test_random_configuration_matches_oracle(dev, c):
             rc_codes, rc_scales = oracle.qwz_quantize(ref[3])
             assert np.array_equal(codes.cpu().numpy(), rc_codes)
             assert np.array_equal(scales.cpu().numpy().view(np.uint32), rc_scales.view(np.uint32))
+
+
+def _gather_cases():
+    rng = np.random.default_rng(0xF033)
+    out = []
+    for i in range(24):
+        n_ranks = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 33, 64]))
+        align = int(2 ** rng.integers(3, 10))      # the gathers take shard lengths in multiples of 8
+        psi = max(1, int(np.exp(rng.uniform(0.0, np.log(4_000_000)))))
+        out.append(dict(case=i, psi=psi, n_ranks=n_ranks, align=align, qwz=bool(rng.random() < 0.5),
+                        seed=0xF100 + i))
+    return out
+
+
+@pytest.mark.parametrize("c", _gather_cases(),
+                         ids=lambda c: f"case{c['case']}-psi{c['psi']}-N{c['n_ranks']}-a{c['align']}")
+def test_random_gather_matches_oracle(dev, c):
+    """The fp16 or the qwZ-decoding all-gather of a random layout (psi, N,
+    align from 8 to 512): ragged last shards and padding-only shards."""
+    import torch
+    lay = zs.partition_layout(c["psi"], c["n_ranks"], 0, c["align"])
+    L = lay.shard_len
+    say(f"gather fuzz {c}, shard_len={L}")
+    xs = [tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 0.02, c["seed"], tk.STREAM_MASTER + r)
+          for r in range(c["n_ranks"])]
+    replica = torch.empty(c["psi"], dtype=torch.float16, device=dev)
+    if not c["qwz"]:
+        zs.allgather(xs, replica)
+        want = oracle.allgather([host_u16(t) for t in xs], c["psi"])
+    else:
+        codes, scales, dec = [], [], []
+        for x in xs:
+            rc_codes, rc_scales = oracle.qwz_quantize(host_u16(x))
+            codes.append(torch.from_numpy(rc_codes).to(dev))
+            scales.append(torch.from_numpy(rc_scales).to(dev))
+            dec.append(oracle.qwz_dequantize(rc_codes, rc_scales))
+        zs.qwz_allgather(codes, scales, replica)
+        want = oracle.allgather(dec, c["psi"])
+    assert np.array_equal(host_u16(replica), want)
