@@ -14,7 +14,9 @@ from typing import NamedTuple, Sequence
 
 from . import build as _build
 
-LIB_PATH = _build.library_path("libzero_shard.so")
+# ZERO_SHARD_LIBRARY names another build of the same library (for example
+# one with the host code under a sanitizer); by default the in-tree build.
+LIB_PATH = os.environ.get("ZERO_SHARD_LIBRARY") or _build.library_path("libzero_shard.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
