@@ -66,6 +66,19 @@ MUTATIONS = [
     ("qwz scale 255", "const float scale = amax / 127.0f;", "const float scale = amax / 255.0f;", QWZ),
     ("qwz dequant wrong block", "scales[j / ZO_QWZ_BLOCK]", "scales[j / (ZO_QWZ_BLOCK / 2) / 2 + (j % 2)]", QWZ),
     ("memory stage 1", "case 1: return 2.0 * psi + 2.0 * psi + K * psi / n;", "case 1: return 2.0 * psi + K * psi / n;", LM),
+    ("bias correction in float", "s[5] = (float)(1.0 - pow(beta2, (double)step));",
+     "s[5] = 1.0f - powf((float)beta2, (float)step);", ADAM),
+    ("v decays with b1", "const float v1 = b2 * *v + omb2 * (g * g);", "const float v1 = b1 * *v + omb2 * (g * g);", ADAM),
+    ("sqrt before bias correction", "sqrtf(vh) + eps", "sqrtf(v1) / bc2 + eps", ADAM),
+    ("reduce accumulates in double", "float acc = zo_f16_to_f32(slices[0][j]);",
+     "double acc = zo_f16_to_f32(slices[0][j]);", RS),
+    ("qwz scale from the signed maximum", "const float a = fabsf(zo_f16_to_f32(x16[j]));",
+     "const float a = zo_f16_to_f32(x16[j]);", QWZ),
+    # (a clamp at +-128 would change nothing: with scale = max/127 rounded to
+    # nearest, |x/scale| never rounds beyond 127 for finite values)
+    ("qwz clamp at 126", "if (q > 127.0f) q = 127.0f;", "if (q > 126.0f) q = 126.0f;", QWZ),
+    ("allgather copies the padding", "if (flat < psi) replica[flat] = shards[r][j];",
+     "if (flat < psi + 1 && flat < (int64_t)n_ranks * shard_len) replica[flat < psi ? flat : psi - 1] = shards[r][j];", AG),
 ]
 
 
