@@ -141,6 +141,22 @@ def test_fp32_gradient_sequence(dev, qwz):
     assert t_ref == 3
 
 
+def test_empty_shard_still_counts_the_step(dev):
+    """A rank whose shard is empty (psi small against N) still takes part in
+    every step: with len = 0 the call writes no array but counts the step
+    and stores that step's bias corrections, like every other rank."""
+    import torch
+    empty_f32 = torch.empty(0, dtype=torch.float32, device=dev)
+    empty_f16 = torch.empty(0, dtype=torch.float16, device=dev)
+    stats, ws, applied = zs.new_stats(dev), zs.new_workspace(0, dev), zs.new_step_counter(dev)
+    for k in range(3):
+        zs.adam_step_device_t(empty_f16, empty_f32, empty_f32.clone(), empty_f32.clone(), empty_f16.clone(),
+                              applied_steps=applied, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16,
+                              stats=stats, workspace=ws)
+        assert zs.read_stats(stats) == (0, 0.0)
+        _assert_counter(applied, k + 1, k + 1, f"empty shard, call {k}")
+
+
 def test_graph_replayed_across_steps(dev):
     """Statistics + the device-t update captured once; before each replay
     the gradient buffer is refilled in place (eagerly) with the next step's
