@@ -15,7 +15,8 @@ wall time over the K timed steps.  The algorithmic traffic is 30 bytes per
 parameter for the whole call (2 for the statistics pass, 28 for the update).
 
 Also reported: the update kernel alone against the HBM roofline (HIP events
-around each launch, on the launch stream), a plain copy/read kernel as the
+around each launch, on the launch stream), the statistics pass timed the
+same way inside the same steps, a plain copy/read kernel as the
 attainable ceiling, the update with global-norm clipping, the owner-side
 reduce of 64 fp16 slices of the 7.5B / N = 64 shard (117,187,584
 parameters), the fp16 all-gather and the qwZ block-INT8 variants (encoder
