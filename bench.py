@@ -94,12 +94,13 @@ def counter_traffic(path=COUNTERS_FILE):
 def ceiling(torch, tk, dev, n_floats=1 << 30, reps=5):
     """Plain copy (8 B/element), in-place read-modify-write with the
     update's store policy (8 B/element) and read (4 B/element), GB/s."""
+    from zero_partitioned_mixed_flat_amd import probes
     src = torch.ones(n_floats, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     sink = torch.empty(1 << 16, dtype=torch.float32, device=dev)
     out = {}
     for name, fn, bytes_per in (("copy", lambda: tk.copy_f32(src, dst), 8),
-                                ("rmw", lambda: tk.rmw_f32(dst), 8),
+                                ("rmw", lambda: probes.rmw_f32(dst), 8),
                                 ("read", lambda: tk.read_f32(src, sink), 4)):
         fn()
         torch.cuda.synchronize()

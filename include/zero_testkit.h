@@ -1,9 +1,10 @@
 /*
  * zero_testkit.h -- seeded synthetic inputs and plain streaming reference
  * kernels, for the tests and the benchmark of the shard optimizer step.
- * Nothing here computes any part of the optimizer step; the same generated
- * device buffers feed both the HIP library and (after a copy to the host)
- * the CPU oracle.
+ * Nothing here computes any part of the optimizer step or includes the
+ * optimizer library's code (its probes are in zero_probes.h); the same
+ * generated device buffers feed both the HIP library and (after a copy to
+ * the host) the CPU oracle.
  *
  * Generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
  * numbers: as easy as 1, 2, 3", SC'11), a counter-based generator: element j
@@ -62,25 +63,8 @@ int zero_testkit_inject_inf_f16(uint16_t *out, int64_t n, double prob, uint64_t 
  * floor(n/4)*4 floats whose per-block sums go to sink[block] for the blocks
  * below sink_len (4 B per element; at most 4 blocks per CU are launched). */
 int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream_);
-/* In place: p[j] += 1 over the first floor(n/4)*4 floats (8 B of traffic
- * per element), with the optimizer's streaming-store policy: the attainable
- * rate for read-modify-write streams. */
-int zero_testkit_rmw_f32(float *p, int64_t n, hipStream_t stream_);
 int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len,
                           hipStream_t stream_);
-
-/* Device arithmetic check: quot[j] = a[j] / b[j], root[j] = sqrt(a[j]),
- * half[j] = binary16 of a[j] and wide[j] = binary32 of the binary16 code
- * h[j], each with the primitive and build flags of the optimizer library
- * (correctly rounded division and square root, round-to-nearest-even
- * conversion, subnormals kept), for comparison with host IEEE results.  All
- * arrays hold n elements of device memory. */
-int zero_testkit_arith_f32(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot,
-                           float *root, uint16_t *half, float *wide, hipStream_t stream_);
-
-/* out[j] = the optimizer library's device-side bias correction
- * (float)(1 - beta^t[j]) for n device-resident step numbers t. */
-int zero_testkit_bias_correction(double beta, const int64_t *t, int64_t n, float *out, hipStream_t stream_);
 
 /* Text of the HIP error behind the last -4 on the calling thread. */
 const char *zero_testkit_last_error(void);

@@ -24,9 +24,9 @@ def _declared(header):
 def test_every_declared_symbol_is_exported():
     headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
     assert headers
-    from zero_partitioned_mixed_flat_amd import host_adam
+    from zero_partitioned_mixed_flat_amd import host_adam, probes
     libs = {"zero_shard.h": zs.library(), "zero_testkit.h": testkit.library(),
-            "zero_host_adam.h": host_adam.library()}
+            "zero_host_adam.h": host_adam.library(), "zero_probes.h": probes.library()}
     for h in headers:
         names = _declared(h)
         assert names, h
@@ -255,3 +255,34 @@ def test_adam_step_device_t_rejects_bad_arguments():
     assert call(scales=10 * A) == -1
     assert call(dt=5) == -1
     assert call(n=-1) == -1
+
+
+def _includes(path):
+    return set(re.findall(r'^\s*#\s*include\s*[<"]([^>"]+)[>"]', open(path).read(), re.M))
+
+
+def _imports(path):
+    names = set()
+    for line in open(path):
+        m = re.match(r"\s*(?:from\s+(\S+)\s+import|import\s+(\S+))", line)
+        if m:
+            names.add((m.group(1) or m.group(2)).split(".")[0])
+    return names
+
+
+def test_oracle_generators_and_library_share_no_code():
+    """The oracle, the seeded input generators and the HIP library are three
+    separate code bases: no source of one includes or imports another (the
+    probes of the library's own code are built with the library, apart from
+    the generators)."""
+    csrc = os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc")
+    library_headers = {"shard_kernels.hpp", "zero_shard.h", "zero_probes.h", "zero_host_adam.h"}
+    assert _includes(os.path.join(csrc, "testkit.hip")) & (library_headers | {"zero_oracle.h"}) == set()
+    assert _includes(os.path.join(ROOT, "include", "zero_testkit.h")) & library_headers == set()
+    assert _includes(os.path.join(ROOT, "oracle", "zero_oracle.c")) & (library_headers | {"zero_testkit.h"}) == set()
+    assert "zero_partitioned_mixed_flat_amd" not in _imports(os.path.join(ROOT, "oracle", "__init__.py"))
+    for f in ("shard_kernels.hpp", "zero_shard.hip", "probes.hip", "host_adam.cpp"):
+        assert _includes(os.path.join(csrc, f)) & {"zero_oracle.h", "zero_testkit.h"} == set(), f
+    for f in glob.glob(os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "*.py")):
+        assert "oracle" not in _imports(f), f"{f} imports the oracle"
+    assert "testkit" not in " ".join(_imports(os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "_native.py")))

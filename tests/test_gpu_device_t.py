@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import zero_partitioned_mixed_flat_amd as zs
-from zero_partitioned_mixed_flat_amd import testkit as tk
+from zero_partitioned_mixed_flat_amd import probes, testkit as tk
 from gpu_util import assert_state_parity, assert_stats, host_f32, host_u16, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def test_device_bias_corrections_match_oracle(dev, beta):
     import torch
     rng = np.random.default_rng(int(beta * 1e4))
     t = np.concatenate([np.arange(1, 65537), rng.integers(65537, 10**9, 65536)]).astype(np.int64)
-    got = tk.bias_correction(beta, torch.from_numpy(t).to(dev)).cpu().numpy()
+    got = probes.bias_correction(beta, torch.from_numpy(t).to(dev)).cpu().numpy()
     want = np.empty(t.size, dtype=np.float32)
     for i, tt in enumerate(t):
         st, s = oracle.adam_scalars(LR, beta, 0.5, EPS, 1.0, int(tt))

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import zero_partitioned_mixed_flat_amd as zs
-from zero_partitioned_mixed_flat_amd import testkit as tk
+from zero_partitioned_mixed_flat_amd import probes, testkit as tk
 from gpu_util import (assert_state_parity, assert_stats, host_f32, host_u16, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
@@ -406,7 +406,7 @@ def test_device_arithmetic_matches_host_ieee(dev):
     h[:65536] = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     dev_a, dev_b = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
     dev_h = torch.from_numpy(h.view(np.int16)).to(dev)
-    quot, root, half, wide = tk.arith_f32(dev_a, dev_b, dev_h)
+    quot, root, half, wide = probes.arith_f32(dev_a, dev_b, dev_h)
     with np.errstate(all="ignore"):
         want = {"quot": a / b, "root": np.sqrt(a), "half": a.astype(np.float16), "wide": h.view(np.float16).astype(np.float32)}
     got = {"quot": quot.cpu().numpy(), "root": root.cpu().numpy(),
@@ -494,7 +494,7 @@ def test_ceiling_kernels_compute_what_they_claim(dev):
     tk.copy_f32(src, dst)
     assert torch.equal(src, dst)
     before = host_f32(dst)
-    tk.rmw_f32(dst)
+    probes.rmw_f32(dst)
     after = host_f32(dst)
     body = (n // 4) * 4
     assert np.array_equal(after[:body], (before[:body] + np.float32(1.0)).astype(np.float32))

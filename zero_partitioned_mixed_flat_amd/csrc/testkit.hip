@@ -1,13 +1,12 @@
 // testkit.hip -- seeded synthetic inputs (Philox4x32-10 + Box-Muller) and
-// plain streaming reference kernels; see include/zero_testkit.h.  None of
-// this is part of the optimizer step.
+// plain streaming reference kernels; see include/zero_testkit.h.  Nothing
+// here is, or includes, code of the optimizer library.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 
-#include "shard_kernels.hpp"
 #include "zero_testkit.h"
 
 namespace {
@@ -122,7 +121,8 @@ __global__ void inject_inf_kernel(uint16_t *out, int64_t n, double prob, uint64_
 // Reference streaming kernels in the shapes that measured fastest on MI355X:
 // copy = one 16-byte non-temporal load and store per lane, 64-lane blocks,
 // one block per 256 floats; read = four 16-byte non-temporal loads per lane
-// per iteration over a grid of four blocks per CU.
+// per iteration over a grid of four blocks per CU.  (The read-modify-write
+// reference, which uses the library's store policy, is in probes.hip.)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCopyBlock = 64;
 
@@ -132,21 +132,6 @@ __global__ __launch_bounds__(kCopyBlock) void copy_f32_kernel(const f32x4 *__res
   const int64_t i = blockIdx.x * static_cast<int64_t>(kCopyBlock) + threadIdx.x;
   if (i < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
   if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
-}
-
-// In-place read-modify-write of whole 16-byte chunks (x += 1), the access
-// type of the optimizer's state streams: non-temporal loads, and stores
-// through a buffer window with the library's streaming-store policy.
-__global__ __launch_bounds__(kCopyBlock) void rmw_f32_kernel(float *__restrict__ p, int64_t n4) {
-  const int64_t base = blockIdx.x * static_cast<int64_t>(kCopyBlock);
-  if (base >= n4) return;
-  const int64_t i = base + threadIdx.x;
-  const auto w = zs::store_window(p + 4 * base, kCopyBlock * 16);
-  if (i < n4) {
-    zs::f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const zs::f32x4 *>(p) + i);
-    x += 1.0f;
-    zs::window_store(w, threadIdx.x * 16, x);
-  }
 }
 
 __global__ __launch_bounds__(kBlock) void read_f32_kernel(const f32x4 *__restrict__ src, int64_t n4,
@@ -172,27 +157,6 @@ __global__ __launch_bounds__(kBlock) void read_f32_kernel(const f32x4 *__restric
     __syncthreads();
   }
   if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < sink_len) sink[blockIdx.x] = s[0];
-}
-
-// The product's arithmetic primitives, built with the same flags as the
-// library: binary32 division and square root, the binary32 -> binary16
-// conversion of the fp16 write-back and the binary16 -> binary32 decode.
-__global__ void arith_kernel(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot, float *root,
-                             uint16_t *half, float *wide) {
-  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
-       j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    quot[j] = a[j] / b[j];
-    root[j] = __builtin_sqrtf(a[j]);
-    half[j] = static_cast<uint16_t>(zs::f2h(a[j]));
-    wide[j] = zs::h2f(h[j]);
-  }
-}
-
-// The library's device-side bias correction 1 - beta^t for given t.
-__global__ void bias_correction_kernel(double beta, const int64_t *t, int64_t n, float *out) {
-  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
-       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    out[j] = zs::bias_correction(beta, t[j]);
 }
 
 int cu_count() {
@@ -285,18 +249,6 @@ int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s
   return launched();
 }
 
-int zero_testkit_rmw_f32(float *p, int64_t n, hipStream_t stream_) {
-  if (n < 0 || (n > 0 && p == nullptr)) return -1;
-  if (reinterpret_cast<uintptr_t>(p) & 15u) return -1;
-  const int64_t n4 = n / 4;
-  const int64_t blocks = (n4 + kCopyBlock - 1) / kCopyBlock;
-  if (blocks > INT32_MAX) return -1;
-  if (blocks == 0) return 0;
-  clear_stale_error();
-  rmw_f32_kernel<<<static_cast<unsigned>(blocks), kCopyBlock, 0, stream_>>>(p, n4);
-  return launched();
-}
-
 int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len, hipStream_t stream_) {
   if (n < 0 || sink_len < 1 || sink == nullptr || (n > 0 && src == nullptr)) return -1;
   if (reinterpret_cast<uintptr_t>(src) & 15u) return -1;
@@ -306,26 +258,6 @@ int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink
   const int grid = static_cast<int>(need < 1 ? 1 : (need < cap ? need : cap));
   clear_stale_error();
   read_f32_kernel<<<grid, kBlock, 0, stream_>>>(reinterpret_cast<const f32x4 *>(src), n4, sink, sink_len);
-  return launched();
-}
-
-int zero_testkit_arith_f32(const float *a, const float *b, const uint16_t *h, int64_t n, float *quot, float *root,
-                           uint16_t *half, float *wide, hipStream_t stream_) {
-  if (n < 0) return -1;
-  if (n > 0 && (a == nullptr || b == nullptr || h == nullptr || quot == nullptr || root == nullptr ||
-                half == nullptr || wide == nullptr))
-    return -1;
-  if (n == 0) return 0;
-  clear_stale_error();
-  arith_kernel<<<grid_for(n), kBlock, 0, stream_>>>(a, b, h, n, quot, root, half, wide);
-  return launched();
-}
-
-int zero_testkit_bias_correction(double beta, const int64_t *t, int64_t n, float *out, hipStream_t stream_) {
-  if (n < 0 || (n > 0 && (t == nullptr || out == nullptr))) return -1;
-  if (n == 0) return 0;
-  clear_stale_error();
-  bias_correction_kernel<<<grid_for(n), kBlock, 0, stream_>>>(beta, t, n, out);
   return launched();
 }
 

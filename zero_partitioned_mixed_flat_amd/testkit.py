@@ -1,6 +1,8 @@
 """ctypes binding of libzero_testkit.so (include/zero_testkit.h): seeded
-synthetic inputs on the device and streaming reference kernels.  Used by the
-tests and the benchmark; holds none of the optimizer step's arithmetic.
+synthetic inputs on the device and plain streaming reference kernels.  Used
+by the tests and the benchmark; holds none of the optimizer step's
+arithmetic and loads none of the optimizer library's code (the probes of
+that code are in probes.py).
 
 Input recipe of the workloads (sigma is a standard deviation):
   master  ~ N(0, 0.02)           fp32
@@ -37,16 +39,12 @@ _lib.zero_testkit_normal_f16.argtypes = [_p, _i64, _dbl, _u64, _u32, _p]
 _lib.zero_testkit_student_t3_f16.argtypes = [_p, _i64, _dbl, _i32, _u64, _u32, _p]
 _lib.zero_testkit_inject_inf_f16.argtypes = [_p, _i64, _dbl, _u64, _u32, _p]
 _lib.zero_testkit_copy_f32.argtypes = [_p, _p, _i64, _p]
-_lib.zero_testkit_rmw_f32.argtypes = [_p, _i64, _p]
 _lib.zero_testkit_read_f32.argtypes = [_p, _i64, _p, _i32, _p]
-_lib.zero_testkit_arith_f32.argtypes = [_p, _p, _p, _i64, _p, _p, _p, _p, _p]
-_lib.zero_testkit_bias_correction.argtypes = [_dbl, _p, _i64, _p, _p]
 _lib.zero_testkit_last_error.argtypes = []
 _lib.zero_testkit_last_error.restype = ctypes.c_char_p
 for _f in ("zero_testkit_philox", "zero_testkit_normal_f32", "zero_testkit_normal_f16",
            "zero_testkit_student_t3_f16", "zero_testkit_inject_inf_f16", "zero_testkit_copy_f32",
-           "zero_testkit_read_f32", "zero_testkit_arith_f32", "zero_testkit_bias_correction",
-           "zero_testkit_rmw_f32"):
+           "zero_testkit_read_f32"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 # Philox stream ids of the workload tensors
@@ -109,36 +107,9 @@ def copy_f32(src, dst):
     _ok(_lib.zero_testkit_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(), _stream()), "copy_f32")
 
 
-def rmw_f32(p):
-    _ok(_lib.zero_testkit_rmw_f32(p.data_ptr(), p.numel(), _stream()), "rmw_f32")
-
-
 def read_f32(src, sink):
     _ok(_lib.zero_testkit_read_f32(src.data_ptr(), src.numel(), sink.data_ptr(), sink.numel(), _stream()),
         "read_f32")
-
-
-def bias_correction(beta: float, t):
-    """The library's device-side (float)(1 - beta^t) for an int64 device tensor t."""
-    import torch
-    assert t.dtype == torch.int64 and t.is_contiguous()
-    out = torch.empty(t.numel(), dtype=torch.float32, device=t.device)
-    _ok(_lib.zero_testkit_bias_correction(float(beta), t.data_ptr(), t.numel(), out.data_ptr(), _stream()),
-        "bias_correction")
-    return out
-
-
-def arith_f32(a, b, h):
-    """(a / b, sqrt(a), f16(a) bits, f32(h)) on the device with the library's
-    primitives; a, b float32 and h int16 (fp16 bits) device tensors of one length."""
-    import torch
-    n = a.numel()
-    assert b.numel() == n and h.numel() == n and a.dtype == b.dtype == torch.float32 and h.dtype == torch.int16
-    quot, root, wide = (torch.empty_like(a) for _ in range(3))
-    half = torch.empty(n, dtype=torch.int16, device=a.device)
-    _ok(_lib.zero_testkit_arith_f32(a.data_ptr(), b.data_ptr(), h.data_ptr(), n, quot.data_ptr(), root.data_ptr(),
-                                    half.data_ptr(), wide.data_ptr(), _stream()), "arith_f32")
-    return quot, root, half, wide
 
 
 def init_shard_state(length: int, seed: int, *, zero_moments: bool, device="cuda"):
