@@ -529,7 +529,12 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(upd_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "avg_launch_ms": round(upd_avg_s * 1e3, 4),
                      "median_launch_ms": round(upd_median_ms, 4), "min_launch_ms": round(upd_sorted[0], 4),
-                     "algorithmic_bytes_per_launch": UPDATE_BYTES_PER_PARAM * L},
+                     "algorithmic_bytes_per_launch": UPDATE_BYTES_PER_PARAM * L,
+                     # the same-box ceiling of an in-place read-modify-write stream
+                     # (measured in this run), which cancels box-to-box spread
+                     "rmw_ceiling_gbps": ceil.get("rmw_gbps"),
+                     "frac_of_rmw_ceiling": (round(upd_gbps / ceil["rmw_gbps"], 4) if ceil.get("rmw_gbps")
+                                             else None)},
         "statistics": {"kernels": "grad_stats_kernel<f16> + finalize_stats_kernel", "bound": "hbm",
                        "avg_ms": round(stats_avg_s * 1e3, 4),
                        "achieved": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9, 1), "unit": "GB/s",
