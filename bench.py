@@ -343,16 +343,26 @@ def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
     g_h = g[:n].cpu().view(torch.int16).numpy().view(np.uint16).copy()
     st = [master[:n].cpu().numpy().copy(), m[:n].cpu().numpy().copy(), v[:n].cpu().numpy().copy(),
           p16[:n].cpu().view(torch.int16).numpy().view(np.uint16).copy()]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        rc, _, _ = oracle.shard_adam_step(g_h, *st, step=T0 + reps, lr=LR, beta1=BETAS[0], beta2=BETAS[1],
-                                          eps=EPS, inv_scale=INV_SCALE)
-        assert rc == 0
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
+    # the oracle is single-threaded: pin it to one host core while it runs
+    pinned = None
+    if hasattr(os, "sched_getaffinity"):
+        allowed = os.sched_getaffinity(0)
+        pinned = min(allowed)
+        os.sched_setaffinity(0, {pinned})
+    try:
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            rc, _, _ = oracle.shard_adam_step(g_h, *st, step=T0 + reps, lr=LR, beta1=BETAS[0], beta2=BETAS[1],
+                                              eps=EPS, inv_scale=INV_SCALE)
+            assert rc == 0
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s:
+                break
+    finally:
+        if pinned is not None:
+            os.sched_setaffinity(0, allowed)
     cpu_model = platform.processor() or "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -362,10 +372,12 @@ def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
                     break
     except OSError:
         pass
-    return {"value": n * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+    rate = n * reps / el
+    return {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n:,} params of the 375,000,064-param shard, statistics + update, "
                       f"{reps} repetitions in {el:.1f} s",
-            "host_cpu": cpu_model, "host_threads": os.cpu_count()}
+            "gbps": round(rate * (UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) / 1e9, 2),
+            "pinned_core": pinned, "host_cpu": cpu_model, "host_threads": os.cpu_count()}
 
 
 def host_adam_secondary(torch, g, master, m, v, p16, steps=3):
@@ -509,6 +521,7 @@ def main():
     host = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(torch, g, master, m, v, p16)
+        cpu["gpu_over_oracle"] = round(value / cpu["value"], 1)
         log(f"cpu baseline: {cpu}")
         host = host_adam_secondary(torch, g, master, m, v, p16)
         log(f"host SIMD step: {host}")
