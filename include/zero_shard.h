@@ -27,6 +27,9 @@
  *     make that first call outside HIP graph capture.  After it, every call
  *     enqueues kernels only (no memset, copy or allocation) and can be
  *     captured into a graph.
+ *   - Arrays a call writes (outputs, the statistics, the workspace) must not
+ *     share a byte with any other array of the same call
+ *     (ZERO_ERR_INVALID_ARG otherwise).
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and the call returns without synchronising; outputs, including
  *     the device-resident zero_grad_stats_t, are valid once the stream has
@@ -48,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 5
+#define ZERO_SHARD_ABI_VERSION 6
 /* Largest number of simulated rank slices one reduce call accepts. */
 #define ZERO_MAX_SLICES 64
 /* Values per qwZ quantization block (one binary32 scale each). */

@@ -21,9 +21,19 @@ def _declared(header):
     return DECL.findall(open(header).read())
 
 
+CSRC = os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc")
+
+
+def test_public_headers_are_the_product_boundary():
+    """include/ holds the product's C ABI only; the generators' and the
+    probes' headers sit with their sources."""
+    names = sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert names == ["zero_host_adam.h", "zero_shard.h"]
+
+
 def test_every_declared_symbol_is_exported():
     headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
-    assert headers
+    headers += [os.path.join(CSRC, "zero_testkit.h"), os.path.join(CSRC, "zero_probes.h")]
     from zero_partitioned_mixed_flat_amd import host_adam, probes
     libs = {"zero_shard.h": zs.library(), "zero_testkit.h": testkit.library(),
             "zero_host_adam.h": host_adam.library(), "zero_probes.h": probes.library()}
@@ -40,8 +50,8 @@ def test_shard_header_declares_the_path():
     assert {"zero_partition_layout", "zero_model_state_bytes", "zero_workspace_bytes",
             "zero_shard_grad_reduce", "zero_shard_grad_stats", "zero_shard_adam_step",
             "zero_shard_allgather", "zero_shard_adam_step_qwz", "zero_qwz_quantize", "zero_qwz_allgather",
-            "zero_shard_adam_step_device_t", "zero_status_string", "zero_last_error",
-            "zero_shard_abi_version"} <= names
+            "zero_shard_adam_step_device_t", "zero_status_string",
+            "zero_last_error", "zero_shard_abi_version"} <= names
 
 
 def test_abi_version_matches_header():
@@ -126,6 +136,10 @@ def _adam(lib, **kw):
     (dict(s=float("inf")), -1), (dict(m=3 * A + 4), -2), (dict(p16=5 * A + 8), -2),
     (dict(m=2 * A + 64), -1),                       # exp_avg overlaps master
     (dict(pre=0, ws=None), -1), (dict(pre=0, wsn=16), -3), (dict(pre=0, ws=7 * A + 8), -2),
+    (dict(stats=2 * A + 96), -1),                   # stats inside master
+    (dict(stats=A + 64), -1),                       # stats inside the gradient
+    (dict(pre=0, ws=3 * A + 128), -1),              # workspace inside exp_avg
+    (dict(pre=0, ws=6 * A - 1024, wsn=1 << 16), -1),  # workspace covers stats
 ])
 def test_adam_step_rejects_bad_arguments(kw, status):
     lib = zs.library()
@@ -148,7 +162,16 @@ def test_reduce_and_stats_reject_bad_arguments():
     assert f(ptrs, 4, 10, out, 200 * A, 1.0, 300 * A, 8, None) == -3    # short workspace
     bad = (ctypes.c_void_p * 2)(A, A + 2)
     assert f(bad, 2, 10, out, None, 1.0, None, 0, None) == -2           # misaligned slice
+    big = 1 << 16
+    assert f(ptrs, 4, 10, out, 300 * A, 1.0, 300 * A - 1024, big, None) == -1   # workspace covers stats
+    assert f(ptrs, 4, 10, out, 300 * A, 1.0, out, big, None) == -1              # workspace on out_sum
+    assert f(ptrs, 4, 10, out, out + 16, 1.0, 300 * A, big, None) == -1         # stats inside out_sum
+    assert f(ptrs, 4, 10, out, A, 1.0, 300 * A, big, None) == -1                # stats on slice 0
+    assert f(ptrs, 4, 10, out, 300 * A, 1.0, 2 * A, big, None) == -1            # workspace on slice 1
     g = lib.zero_shard_grad_stats
+    assert g(A, 1, 100, 1.0, A + 32, 3 * A, 1 << 16, None) == -1       # stats inside grad
+    assert g(A, 1, 100, 1.0, 2 * A, A, 1 << 16, None) == -1            # workspace on grad
+    assert g(A, 1, 100, 1.0, 2 * A, 2 * A - 1024, 1 << 16, None) == -1  # workspace covers stats
     assert g(A, 1, -5, 1.0, 2 * A, 3 * A, 1 << 16, None) == -1
     assert g(A, 9, 5, 1.0, 2 * A, 3 * A, 1 << 16, None) == -1
     assert g(A, 1, 5, float("nan"), 2 * A, 3 * A, 1 << 16, None) == -1
@@ -278,7 +301,7 @@ def test_oracle_generators_and_library_share_no_code():
     csrc = os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc")
     library_headers = {"shard_kernels.hpp", "zero_shard.h", "zero_probes.h", "zero_host_adam.h"}
     assert _includes(os.path.join(csrc, "testkit.hip")) & (library_headers | {"zero_oracle.h"}) == set()
-    assert _includes(os.path.join(ROOT, "include", "zero_testkit.h")) & library_headers == set()
+    assert _includes(os.path.join(csrc, "zero_testkit.h")) & library_headers == set()
     assert _includes(os.path.join(ROOT, "oracle", "zero_oracle.c")) & (library_headers | {"zero_testkit.h"}) == set()
     assert "zero_partitioned_mixed_flat_amd" not in _imports(os.path.join(ROOT, "oracle", "__init__.py"))
     for f in ("shard_kernels.hpp", "zero_shard.hip", "probes.hip", "host_adam.cpp"):

@@ -163,8 +163,11 @@ def test_clipping_with_given_global_stats(dev, n, max_norm):
 
 
 def test_clipping_end_to_end(dev):
-    """Statistics computed by the GPU, clipping active: within the parity bar
-    (the GPU's and the oracle's sums of squares differ by summation order)."""
+    """Statistics computed by the GPU, clipping active.  The GPU's and the
+    oracle's sums of squares may differ in the last bits (summation order);
+    the clipped step depends on them only through the binary32 multiplier
+    (float)(inv_scale * max_norm / sqrt(sumsq)).  For this input both sums
+    give the same multiplier (asserted), so the step is bit-exact."""
     n = 250_003
     master, m, v, p16 = _state(n, 31, False, dev)
     g = _grad16(n, 31, dev)
@@ -179,8 +182,11 @@ def test_clipping_end_to_end(dev):
                                              inv_scale=S16, max_norm=0.05)
     assert rc == 0 and np.sqrt(rssq) > 0.05
     assert_stats(got_stats, (rflag, rssq), "clip e2e")
+    mult = [np.float32(S16 * oracle.clip_factor(x, 0.05)) for x in (got_stats[1], rssq)]
+    assert mult[0] == mult[1], f"clip multipliers differ: {mult}"
     counts = assert_state_parity(_host_state(master, m, v, p16), ref, "clip e2e")
     say("  inexact elements:", counts)
+    assert sum(counts.values()) == 0
 
 
 @pytest.mark.parametrize("n_slices", [1, 2, 3, 8, 9, 17, 64])
@@ -503,3 +509,43 @@ def test_ceiling_kernels_compute_what_they_claim(dev):
     tk.read_f32(src, sink)
     total = float(sink.double().sum())
     assert abs(total - float(src[:body].double().sum())) <= 1e-3 * float(src[:body].abs().double().sum())
+
+
+def test_explicit_stream_without_workspace(dev):
+    """Calls given another stream and no workspace allocate a temporary one
+    that the caching allocator must not hand out again before that stream
+    has used it: tensors allocated and filled right after the calls on the
+    current stream must not disturb the statistics, and the results must
+    equal those of the same calls on the current stream."""
+    import torch
+    n = 300_001
+    g = _grad16(n, 0x57, dev)
+    slices = [_grad16(n, 0x57, dev, stream=tk.STREAM_GRAD + 1 + r) for r in range(4)]
+    a = list(_state(n, 0x57, False, dev))
+    b = [t.clone() for t in a]
+    sa, sb, sr, srb = (zs.new_stats(dev) for _ in range(4))
+    out_a = torch.empty(n, dtype=torch.float32, device=dev)
+    out_b = torch.empty_like(out_a)
+    kw = dict(step=5, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16, max_grad_norm=0.05)
+    zs.adam_step(g, *a, stats=sa, **kw)
+    zs.grad_reduce(slices, out_a, stats=sr, inv_grad_scale=S16 / 4)
+    ga = zs.new_stats(dev)
+    zs.grad_stats(g, ga, inv_grad_scale=S16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    gb = zs.new_stats(dev)
+    zs.adam_step(g, *b, stats=sb, stream=side, **kw)
+    zs.grad_reduce(slices, out_b, stats=srb, inv_grad_scale=S16 / 4, stream=side)
+    zs.grad_stats(g, gb, inv_grad_scale=S16, stream=side)
+    # allocations on the current stream right away: without the recorded
+    # stream they could reuse the temporaries while the side stream runs
+    junk = [torch.full((zs.workspace_bytes(n),), 0x7F, dtype=torch.uint8, device=dev) for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    for x, y in ((sa, sb), (sr, srb), (ga, gb)):
+        assert zs.read_stats(x) == zs.read_stats(y)
+    assert torch.equal(out_a.view(torch.int32), out_b.view(torch.int32))
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))

@@ -17,14 +17,16 @@ All device work runs in the HIP library ``libzero_shard.so`` (C ABI in
 ``include/zero_shard.h``); this package only marshals arguments.
 """
 from ._native import (  # noqa: F401
-    STATS_BYTES, ZERO_F16, ZERO_F32, ZERO_MAX_SLICES, ZERO_QWZ_BLOCK, Layout, ZeroError, adam_step,
-    adam_step_device_t, allgather, new_step_counter, read_step_counter, grad_reduce, grad_stats, library, model_state_bytes, new_stats, new_workspace,
-    partition_layout, qwz_allgather, qwz_quantize, qwz_scales_len, read_stats, workspace_bytes)
+    STATS_BYTES, ZERO_F16, ZERO_F32, ZERO_MAX_SLICES, ZERO_QWZ_BLOCK, Layout,
+    ZeroError, adam_step, adam_step_device_t, allgather, grad_reduce, grad_stats, library,
+    model_state_bytes, new_stats, new_step_counter, new_workspace, partition_layout, qwz_allgather, qwz_quantize,
+    qwz_scales_len, read_stats, read_step_counter, workspace_bytes)
 
 __all__ = [
     "Layout", "ZeroError", "partition_layout", "model_state_bytes", "workspace_bytes",
     "new_workspace", "new_stats", "read_stats", "grad_reduce", "grad_stats", "adam_step", "allgather",
     "adam_step_device_t", "new_step_counter", "read_step_counter",
     "qwz_quantize", "qwz_allgather", "qwz_scales_len",
-    "library", "ZERO_F16", "ZERO_F32", "ZERO_MAX_SLICES", "ZERO_QWZ_BLOCK", "STATS_BYTES",
+    "library", "ZERO_F16", "ZERO_F32", "ZERO_MAX_SLICES", "ZERO_QWZ_BLOCK",
+    "STATS_BYTES",
 ]

@@ -31,7 +31,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 # the version of include/zero_shard.h this binding is written against
-ZERO_SHARD_ABI_VERSION = 5
+ZERO_SHARD_ABI_VERSION = 6
 _lib.zero_shard_abi_version.argtypes = []
 _lib.zero_shard_abi_version.restype = ctypes.c_int
 if _lib.zero_shard_abi_version() != ZERO_SHARD_ABI_VERSION:
@@ -180,6 +180,17 @@ def new_workspace(length: int, device=None):
     return torch.empty(max(workspace_bytes(length), 16), dtype=torch.uint8, device=device or "cuda")
 
 
+def _temp_workspace(length: int, device, stream):
+    """A workspace for one call.  It is freed when the call returns, while
+    the kernels may still use it on `stream`; recording that stream keeps the
+    caching allocator from handing the block to another allocation until the
+    stream has passed this point."""
+    ws = new_workspace(length, device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
 def _grad_dtype(grad) -> int:
     torch = _torch()
     if grad.dtype == torch.float16:
@@ -206,7 +217,7 @@ def grad_reduce(slices: Sequence, out, *, stats=None, inv_grad_scale: float = 1.
     if stats is not None:
         stats_p = _dev_ptr(stats, None, "stats")
         if workspace is None:
-            workspace = new_workspace(length, out.device)
+            workspace = _temp_workspace(length, out.device, stream)
         ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
     _check(_lib.zero_shard_grad_reduce(ctypes.cast(ptrs, ctypes.c_void_p), n, length, out_p, stats_p,
                                        float(inv_grad_scale), ws_p, ws_n, _stream(stream)))
@@ -230,7 +241,7 @@ def grad_stats(grad, stats, *, inv_grad_scale: float, workspace=None, stream=Non
     length = grad.numel()
     g_p = _dev_ptr(grad, None, "grad")
     if workspace is None:
-        workspace = new_workspace(length, grad.device)
+        workspace = _temp_workspace(length, grad.device, stream)
     _check(_lib.zero_shard_grad_stats(g_p, _grad_dtype(grad), length, float(inv_grad_scale),
                                       _dev_ptr(stats, None, "stats"), _dev_ptr(workspace, None, "workspace"),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -255,7 +266,7 @@ def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: floa
     ws_p, ws_n = None, 0
     if not stats_precomputed:
         if workspace is None:
-            workspace = new_workspace(length, master.device)
+            workspace = _temp_workspace(length, master.device, stream)
         ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
     tail = (length, int(step), ctypes.byref(hp), _dev_ptr(stats, None, "stats"), int(bool(stats_precomputed)),
             ws_p, ws_n, _stream(stream))
@@ -306,7 +317,7 @@ def adam_step_device_t(grad, master, exp_avg, exp_avg_sq, param16, *, applied_st
     ws_p, ws_n = None, 0
     if not stats_precomputed:
         if workspace is None:
-            workspace = new_workspace(length, master.device)
+            workspace = _temp_workspace(length, master.device, stream)
         ws_p, ws_n = _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
     _check(_lib.zero_shard_adam_step_device_t(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *q, length,
                                               _dev_ptr(applied_steps, torch.int64, "applied_steps", 2),

@@ -3,10 +3,10 @@ host library with g++.
 
 ``libzero_shard.so``     the C ABI of include/zero_shard.h (the optimizer step)
 ``libzero_testkit.so``   seeded synthetic inputs and plain streaming
-                         reference kernels (include/zero_testkit.h), used by
+                         reference kernels (csrc/zero_testkit.h), used by
                          tests and benchmarks
 ``libzero_probes.so``    device probes of the optimizer library's own code
-                         (include/zero_probes.h), used by tests and benchmarks
+                         (csrc/zero_probes.h), used by tests and benchmarks
 ``libzero_host_adam.so`` the multi-core SIMD host step (include/zero_host_adam.h)
 
 Flags: no FMA contraction, no fast-math (IEEE division and square root stay

@@ -1,6 +1,6 @@
 // probes.hip -- device probes of the optimizer library's own code (its
 // arithmetic helpers and its streaming-store policy); see
-// include/zero_probes.h.  Used by the tests and the benchmark only.
+// zero_probes.h.  Used by the tests and the benchmark only.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

@@ -477,8 +477,9 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
 
 // --------------------------------------------------------------- all-gather
 // Concatenation of N fp16 shards into the flat replica: block (x, y) copies
-// tile x of shard y, 16 bytes (8 values) per lane with non-temporal access;
-// only the part of the shard below psi is copied.
+// tile x of shard y (and every gridDim.x-th tile after it, when the shard has
+// more tiles than one launch may have blocks), 16 bytes (8 values) per lane
+// with non-temporal access; only the part of the shard below psi is copied.
 constexpr int kGatherBlock = 64;
 constexpr int kGatherU = 1;
 constexpr int64_t kGatherTile = static_cast<int64_t>(kGatherBlock) * 8 * kGatherU;
@@ -487,21 +488,23 @@ __global__ __launch_bounds__(kGatherBlock) void allgather_kernel(SliceTable tab,
   const int r = blockIdx.y;
   const int64_t first = static_cast<int64_t>(r) * shard_len;
   const int64_t real = psi - first < shard_len ? psi - first : shard_len;
-  const int64_t tbase = static_cast<int64_t>(blockIdx.x) * kGatherTile;
-  if (tbase >= real) return;
-  const uint16_t *src = tab.p[r] + tbase;
-  uint16_t *dst = replica + first + tbase;
   const uint32_t lane = threadIdx.x * 8;
-  if (tbase + kGatherTile <= real) {
-    u32x4 x[kGatherU];
+  for (int64_t tbase = static_cast<int64_t>(blockIdx.x) * kGatherTile; tbase < real;
+       tbase += static_cast<int64_t>(gridDim.x) * kGatherTile) {
+    const uint16_t *src = tab.p[r] + tbase;
+    uint16_t *dst = replica + first + tbase;
+    if (tbase + kGatherTile <= real) {
+      u32x4 x[kGatherU];
 #pragma unroll
-    for (int k = 0; k < kGatherU; ++k)
-      x[k] = stream_load(reinterpret_cast<const u32x4 *>(src + lane + k * kGatherBlock * 8));
+      for (int k = 0; k < kGatherU; ++k)
+        x[k] = stream_load(reinterpret_cast<const u32x4 *>(src + lane + k * kGatherBlock * 8));
 #pragma unroll
-    for (int k = 0; k < kGatherU; ++k) stream_store(reinterpret_cast<u32x4 *>(dst + lane + k * kGatherBlock * 8), x[k]);
-  } else {
-    const int64_t rem = real - tbase;
-    for (int64_t j = threadIdx.x; j < rem; j += kGatherBlock) dst[j] = src[j];
+      for (int k = 0; k < kGatherU; ++k)
+        stream_store(reinterpret_cast<u32x4 *>(dst + lane + k * kGatherBlock * 8), x[k]);
+    } else {
+      const int64_t rem = real - tbase;
+      for (int64_t j = threadIdx.x; j < rem; j += kGatherBlock) dst[j] = src[j];
+    }
   }
 }
 

@@ -1,5 +1,5 @@
 // testkit.hip -- seeded synthetic inputs (Philox4x32-10 + Box-Muller) and
-// plain streaming reference kernels; see include/zero_testkit.h.  Nothing
+// plain streaming reference kernels; see zero_testkit.h.  Nothing
 // here is, or includes, code of the optimizer library.
 #include <hip/hip_runtime.h>
 

@@ -99,6 +99,11 @@ int cu_count(int *out) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 
+// Most blocks of `block` threads one launch may have along x: HIP takes the
+// grid's size in work-items as a 32-bit count.  The kernels that could need
+// more tiles than this walk the rest with a grid-stride loop.
+constexpr int64_t max_grid_x(int block) { return static_cast<int64_t>(UINT32_MAX) / block; }
+
 // Dynamic LDS bytes per block that leave room for exactly `target` resident
 // blocks of `kernel` on a CU (0 when the kernel's own resources already allow
 // no more than that, or when no size gives exactly `target`).  Found once per
@@ -293,6 +298,10 @@ int zero_shard_grad_stats(const void *grad, int32_t grad_dtype, int64_t len, dou
   if (!aligned16(grad) || !aligned16(stats) || !aligned16(ws))
     return fail(ZERO_ERR_MISALIGNED, "grad_stats: device pointers must be 16-byte aligned");
   if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "grad_stats: workspace too small");
+  const size_t gbytes = static_cast<size_t>(len) * (grad_dtype == ZERO_F16 ? 2 : 4);
+  if (overlap(grad, gbytes, stats, sizeof(zero_grad_stats_t)) || overlap(grad, gbytes, ws, ws_bytes) ||
+      overlap(stats, sizeof(zero_grad_stats_t), ws, ws_bytes))
+    return fail(ZERO_ERR_INVALID_ARG, "grad_stats: grad, stats and workspace must not overlap");
   const int st = launch_stats(grad, grad_dtype == ZERO_F16 ? ZERO_F16 : ZERO_F32, len,
                               static_cast<float>(inv_grad_scale), stats, ws, stream);
   return st == ZERO_OK ? ok() : st;
@@ -323,10 +332,20 @@ int zero_shard_grad_reduce(const uint16_t *const *slices, int32_t n_slices, int6
     if (!aligned16(stats) || !aligned16(ws))
       return fail(ZERO_ERR_MISALIGNED, "grad_reduce: stats/workspace misaligned");
     if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "grad_reduce: workspace too small");
+    // the statistics and the workspace are written: they may share no byte
+    // with each other, the sum or a slice
+    const size_t sb = sizeof(zero_grad_stats_t), ob = static_cast<size_t>(len) * 4;
+    if (overlap(stats, sb, ws, ws_bytes) || overlap(stats, sb, out_sum, ob) || overlap(ws, ws_bytes, out_sum, ob))
+      return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: stats, workspace and out_sum must not overlap");
+    for (int r = 0; r < n_slices; ++r)
+      if (overlap(slices[r], static_cast<size_t>(len) * 2, stats, sb) ||
+          overlap(slices[r], static_cast<size_t>(len) * 2, ws, ws_bytes))
+        return fail(ZERO_ERR_INVALID_ARG, "grad_reduce: stats or workspace overlaps slice %d", r);
   }
-  // one block per tile: every block writes its own partial
-  const int64_t nparts = reduce_partials(len);
-  if (nparts > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "grad_reduce: len too large");
+  // one block per tile (each writes its own partial); beyond the launch
+  // limit the blocks take several tiles each
+  const int64_t tiles = reduce_partials(len);
+  const int64_t nparts = tiles < max_grid_x(zs::kReduceBlock) ? tiles : max_grid_x(zs::kReduceBlock);
   const unsigned grid = static_cast<unsigned>(nparts);
   const float s = static_cast<float>(inv_grad_scale);
   int st;
@@ -380,9 +399,9 @@ int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks, int64_t
   }
   if (psi == 0 || shard_len == 0) return ok();
   const int64_t tiles = ceil_div(shard_len, zs::kGatherTile);
-  if (tiles > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "allgather: shard_len too large");
+  const int64_t gx = tiles < max_grid_x(zs::kGatherBlock) ? tiles : max_grid_x(zs::kGatherBlock);
   clear_stale_error();
-  zs::allgather_kernel<<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(n_ranks)), zs::kGatherBlock, 0,
+  zs::allgather_kernel<<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(n_ranks)), zs::kGatherBlock, 0,
                          stream>>>(tab, shard_len, psi, replica);
   const int st = check_launch("allgather_kernel");
   return st == ZERO_OK ? ok() : st;
@@ -407,7 +426,7 @@ int launch_update(CapKernel cap, const void *grad, float *master, float *m, floa
   constexpr int cap_blocks = QWZ ? kUpdateQwzBlocksPerCU : kUpdateBlocksPerCU;
   constexpr int64_t tile = static_cast<int64_t>(zs::kUpdateBlock) * zs::kChunk * U;
   const int64_t tiles = ceil_div(len, tile);
-  const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
+  const unsigned grid = static_cast<unsigned>(tiles < max_grid_x(zs::kUpdateBlock) ? tiles : max_grid_x(zs::kUpdateBlock));
   size_t lds = 0;
   const int st = occupancy_cap_lds(cap, zs::adam_update_kernel<DT, U, QWZ, DEV_T>, zs::kUpdateBlock, cap_blocks, &lds);
   if (st != ZERO_OK) return st;
@@ -450,24 +469,29 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   if (!aligned16(grad) || !aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
       !aligned16(param16) || !aligned16(stats) || !aligned16(codes) || !aligned16(scales))
     return fail(ZERO_ERR_MISALIGNED, "adam_step: device pointers must be 16-byte aligned");
-  const size_t n = static_cast<size_t>(len);
-  const size_t gbytes = n * (grad_dtype == ZERO_F16 ? 2 : 4);
-  // the arrays, then the qwZ outputs, then the step counter, when present
-  const void *arr[8] = {grad, master, exp_avg, exp_avg_sq, param16, codes, scales, applied};
-  const size_t sz[8] = {gbytes, n * 4, n * 4, n * 4, n * 2, qwz ? n : 0,
-                        qwz ? static_cast<size_t>(qwz_scales_len(len)) * 4 : 0,
-                        dev_t ? sizeof(zero_step_counter_t) : 0u};
-  for (int a = 0; a < 8; ++a)
-    for (int b = a + 1; b < 8; ++b)
-      if (overlap(arr[a], sz[a], arr[b], sz[b])) return fail(ZERO_ERR_INVALID_ARG, "adam_step: arrays overlap");
-  if (dev_t && (overlap(applied, sizeof(zero_step_counter_t), stats, sizeof(zero_grad_stats_t)) ||
-                (!stats_precomputed && overlap(applied, sizeof(zero_step_counter_t), ws, ws_bytes))))
-    return fail(ZERO_ERR_INVALID_ARG, "adam_step: step counter overlaps the statistics or the workspace");
   if (!stats_precomputed) {
     if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: workspace is NULL");
     if (!aligned16(ws)) return fail(ZERO_ERR_MISALIGNED, "adam_step: workspace misaligned");
-    if (ws_bytes < zero_workspace_bytes(len)) return fail(ZERO_ERR_WORKSPACE, "adam_step: workspace too small");
+    if (ws_bytes < zero_workspace_bytes(len))
+      return fail(ZERO_ERR_WORKSPACE, "adam_step: workspace of %zu bytes, %zu needed", ws_bytes,
+                  zero_workspace_bytes(len));
   }
+  const size_t n = static_cast<size_t>(len);
+  const size_t gbytes = n * (grad_dtype == ZERO_F16 ? 2 : 4);
+  // the arrays, the qwZ outputs, the step counter, the statistics and the
+  // workspace (the last three when present): no two may share a byte
+  constexpr int kArgs = 10;
+  const void *arr[kArgs] = {grad, master, exp_avg, exp_avg_sq, param16, codes, scales, applied, stats, ws};
+  const size_t sz[kArgs] = {gbytes, n * 4, n * 4, n * 4, n * 2, qwz ? n : 0,
+                            qwz ? static_cast<size_t>(qwz_scales_len(len)) * 4 : 0,
+                            dev_t ? sizeof(zero_step_counter_t) : 0u, sizeof(zero_grad_stats_t),
+                            stats_precomputed ? 0u : ws_bytes};
+  static const char *const names[kArgs] = {"grad", "master", "exp_avg", "exp_avg_sq", "param16",
+                                           "qwZ codes", "qwZ scales", "step counter", "stats", "workspace"};
+  for (int a = 0; a < kArgs; ++a)
+    for (int b = a + 1; b < kArgs; ++b)
+      if (overlap(arr[a], sz[a], arr[b], sz[b]))
+        return fail(ZERO_ERR_INVALID_ARG, "adam_step: %s overlaps %s", names[a], names[b]);
 
   // Per-step scalars: each is evaluated in double and rounded once to float.
   zs::StepScalars c;
@@ -525,7 +549,8 @@ int zero_shard_adam_step(const void *grad, int32_t grad_dtype, double inv_grad_s
                          const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, false, nullptr,
-                        nullptr, len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+                        nullptr, len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes,
+                        stream);
 }
 
 int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
@@ -533,7 +558,8 @@ int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_gr
                              int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
                              int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, true, codes, scales,
-                        len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+                        len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes,
+                        stream);
 }
 
 int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
@@ -546,7 +572,8 @@ int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype, double i
     return fail(ZERO_ERR_INVALID_ARG, "adam_step_device_t: qwZ codes and scales go together");
   const bool qwz = codes != nullptr;
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, qwz, codes, scales,
-                        len, 1, applied_steps, hp, stats, stats_precomputed, ws, ws_bytes, stream);
+                        len, 1, applied_steps, hp, stats, stats_precomputed, ws, ws_bytes,
+                        stream);
 }
 
 int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes, float *scales, hipStream_t stream) {
@@ -562,7 +589,7 @@ int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes, float *sc
   if (len == 0) return ok();
   constexpr int64_t tile = static_cast<int64_t>(zs::kQwzRow) * kQwzEncU;
   const int64_t tiles = ceil_div(len, tile);
-  const int grid = static_cast<int>(tiles < INT32_MAX ? tiles : INT32_MAX);
+  const unsigned grid = static_cast<unsigned>(tiles < max_grid_x(zs::kWave) ? tiles : max_grid_x(zs::kWave));
   clear_stale_error();
   zs::qwz_quantize_kernel<kQwzEncU><<<grid, zs::kWave, 0, stream>>>(x16, len, reinterpret_cast<uint8_t *>(codes),
                                                                  scales);

@@ -1,4 +1,4 @@
-"""ctypes binding of libzero_probes.so (include/zero_probes.h): device probes
+"""ctypes binding of libzero_probes.so (csrc/zero_probes.h): device probes
 of the optimizer library's own code -- its arithmetic helpers and its
 streaming-store policy -- for the tests and the benchmark."""
 from __future__ import annotations

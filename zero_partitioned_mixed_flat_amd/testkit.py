@@ -1,4 +1,4 @@
-"""ctypes binding of libzero_testkit.so (include/zero_testkit.h): seeded
+"""ctypes binding of libzero_testkit.so (csrc/zero_testkit.h): seeded
 synthetic inputs on the device and plain streaming reference kernels.  Used
 by the tests and the benchmark; holds none of the optimizer step's
 arithmetic and loads none of the optimizer library's code (the probes of
