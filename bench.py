@@ -13,6 +13,10 @@ the gradient statistics (overflow flag + sum of squares, two kernels) and the
 fused Adam update (one kernel).  ``value`` is shard parameters per second of
 wall time over the K timed steps.  The algorithmic traffic is 30 bytes per
 parameter for the whole call (2 for the statistics pass, 28 for the update).
+The steps take their gradients from three pre-generated buffers in turn, so
+that no step can find an earlier step's gradient in the caches (a real step
+sees a fresh gradient); the same loop over one reused buffer is reported
+beside it.
 
 Also reported: the update kernel alone against the HBM roofline (HIP events
 around each launch, on the launch stream), the statistics pass timed the
@@ -21,9 +25,10 @@ attainable ceiling, the update with global-norm clipping, the owner-side
 reduce of 64 fp16 slices of the 7.5B / N = 64 shard (117,187,584
 parameters), the fp16 all-gather and the qwZ block-INT8 variants (encoder
 fused into the update, encoder alone, decoding all-gather), the step on the
-other workload shapes (tiny, 7.5B / N = 64, 7B / N = 8, 1.5e9 / N = 1), the CPU oracle
-timed on a bounded sample of the same workload on one host core, and the
-multi-core SIMD host step (ZeRO-Offload's CPU Adam) on the whole shard.
+other workload shapes (tiny, 7.5B / N = 64, 7B / N = 8 with its skipped
+step, 1.5e9 / N = 1), the CPU oracle timed on bounded samples of these
+workloads on one host core, and the multi-core SIMD host step
+(ZeRO-Offload's CPU Adam) on the whole shard.
 """
 from __future__ import annotations
 
@@ -57,6 +62,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_flat_amd", "csrc", 
 
 PSI, N_RANKS, RANK, ALIGN = 1_500_000_000, 4, 0, 128
 SEED = 0xC2
+N_GRAD_BUFFERS = 3
 LR, BETAS, EPS, INV_SCALE, T0 = 1e-4, (0.9, 0.999), 1e-8, 2.0 ** -16, 1000
 
 
@@ -185,7 +191,7 @@ def _avg_ms(torch, fn, steps, before=None):
     return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
 
-def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, ws, t0):
+def qwz_secondary(torch, zs, tk, dev, steps, grads, master, m, v, p16, stats, ws, t0):
     """qwZ block-INT8 weights (blocks of 256, one fp32 scale each): the update
     with the encoder fused into its write-back, the encoder alone on the fp16
     shard, and the decoding all-gather of the GPT-2-XL layout."""
@@ -195,13 +201,17 @@ def qwz_secondary(torch, zs, tk, dev, steps, g, master, m, v, p16, stats, ws, t0
     step = [t0]
 
     def fused():
+        g = grads[step[0] % len(grads)]
         zs.adam_step(g, master, m, v, p16, step=step[0], lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
                      stats=stats, stats_precomputed=True, qwz_codes=codes, qwz_scales=scales)
         step[0] += 1
+
+    def before():
+        zs.grad_stats(grads[step[0] % len(grads)], stats, inv_grad_scale=INV_SCALE, workspace=ws)
+    before()
     fused()
     # each fused update follows its statistics pass, as in the step
-    fused_ms = _avg_ms(torch, fused, steps,
-                       before=lambda: zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws))
+    fused_ms = _avg_ms(torch, fused, steps, before=before)
     fused_bytes = UPDATE_BYTES_PER_PARAM + QWZ_BYTES_PER_PARAM
     enc = lambda: zs.qwz_quantize(p16, codes, scales)  # noqa: E731
     enc()
@@ -257,23 +267,37 @@ def other_configs_secondary(torch, zs, tk, dev, steps):
     """The step on the other workload shapes: the tiny one (reduce of 4
     slices + update with the fp32 sum; launch-bound, cache-resident), the
     7.5B / N = 64 shard (reduce of 64 slices + update with the fp32 sum), the
-    7B / N = 8 shard and the unpartitioned 1.5e9 model (statistics + update
-    with the fp16 gradient).  Median and minimum of `steps` timed steps."""
+    7B / N = 8 shard (statistics + update with the fp16 gradient, and the
+    same step on a gradient holding +inf, which is skipped) and the
+    unpartitioned 1.5e9 model.  Median and minimum of `steps` timed steps;
+    the statistics-based steps take their gradient from two buffers in
+    turn, as the headline does from three."""
     out = {}
 
-    def entry(workload, n, bytes_per, fn, t0):
+    def entry(workload, n, bytes_per, fn, t0, reps=steps, warm=3):
         t = [t0]
 
         def run():
             fn(t[0])
             t[0] += 1
-        for _ in range(3):
+        for _ in range(warm):
             run()
-        med, mn = _median_ms(torch, run, steps)
+        med, mn = _median_ms(torch, run, reps)
         gbps = bytes_per * n / (med * 1e-3) / 1e9
         return {"workload": workload, "shard_len": n, "median_ms": round(med, 4), "min_ms": round(mn, 4),
                 "params_per_s": n / (med * 1e-3), "bytes_per_param": bytes_per, "hbm_gbps": round(gbps, 1),
                 "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+    def batch_ms(fn, reps):
+        """Average device time per call over `reps` back-to-back calls."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
     def reduce_step(psi, n_ranks, seed, slice_scale, s, t0, name):
         n = zs.partition_layout(psi, n_ranks, 0, 128).shard_len
@@ -287,38 +311,79 @@ def other_configs_secondary(torch, zs, tk, dev, steps):
             zs.grad_reduce(slices, gsum, stats=stats, inv_grad_scale=s, workspace=ws)
             zs.adam_step(gsum, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=s,
                          stats=stats, stats_precomputed=True)
-        res = entry(name, n, REDUCE_BYTES_PER_PARAM(n_ranks) + 30, fn, t0)
-        if n < (1 << 22):
+        small = n < (1 << 22)
+        res = entry(name, n, REDUCE_BYTES_PER_PARAM(n_ranks) + 30, fn, t0, reps=100 if small else steps,
+                    warm=20 if small else 3)
+        if small:
             # launch-bound: the same calls captured once in a HIP graph and
-            # replayed (the step number is fixed in the captured launch)
+            # replayed (the step number is fixed in the captured launch);
+            # per-call medians from events around each call, and the mean of
+            # 100 back-to-back calls with no events in between
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
-                fn(t0 + 100)
-            for _ in range(3):
+                fn(t0 + 1000)
+            for _ in range(20):
                 graph.replay()
-            med, mn = _median_ms(torch, graph.replay, steps)
+            med, mn = _median_ms(torch, graph.replay, 100)
             res["graph_replay_median_ms"], res["graph_replay_min_ms"] = round(med, 4), round(mn, 4)
+            tt = [t0 + 2000]
+
+            def eager():
+                fn(tt[0])
+                tt[0] += 1
+            res["eager_batch_mean_ms"] = round(batch_ms(eager, 100), 4)
+            res["graph_replay_batch_mean_ms"] = round(batch_ms(graph.replay, 100), 4)
             del graph
         del slices, master, m, v, p16, gsum
         torch.cuda.empty_cache()
         return res
 
-    def stats_step(psi, n_ranks, seed, t0, name, student=False):
+    def stats_step(psi, n_ranks, seed, t0, name, student=False, skip_run=False):
         n = zs.partition_layout(psi, n_ranks, 0, 128).shard_len
         master, m, v, p16 = tk.init_shard_state(n, seed, zero_moments=student, device=dev)
-        g = torch.empty(n, dtype=torch.float16, device=dev)
-        if student:
-            tk.student_t3_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD, redraw_overflow=True)
-        else:
-            tk.normal_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD)
+        gs = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(2)]
+        for k, g in enumerate(gs):
+            if student:
+                tk.student_t3_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD + k, redraw_overflow=True)
+            else:
+                tk.normal_f16_(g, 1e-3 * 65536, seed, tk.STREAM_GRAD + k)
         stats, ws = zs.new_stats(dev), zs.new_workspace(n, dev)
 
         def fn(t):
+            g = gs[t % 2]
             zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
             zs.adam_step(g, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
                          stats=stats, stats_precomputed=True)
         res = entry(name, n, UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM, fn, t0)
-        del master, m, v, p16, g
+        if skip_run:
+            # 0.001% of each gradient set to +inf: the statistics flag the
+            # step and every update block leaves before touching the states
+            for k, g in enumerate(gs):
+                tk.inject_inf_f16_(g, 1e-5, seed + 0xF, tk.STREAM_INF + k)
+            ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            for k in range(steps):
+                g = gs[k % 2]
+                ev[k][0].record()
+                zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
+                ev[k][1].record()
+                zs.adam_step(g, master, m, v, p16, step=t0 + 500, lr=LR, betas=BETAS, eps=EPS,
+                             inv_grad_scale=INV_SCALE, stats=stats, stats_precomputed=True)
+                ev[k][2].record()
+            torch.cuda.synchronize()
+            flag = zs.read_stats(stats)[0]
+
+            def med(xs):
+                xs = sorted(xs)
+                return (xs[(len(xs) - 1) // 2] + xs[len(xs) // 2]) / 2
+            whole = med([a.elapsed_time(c) for a, _, c in ev])
+            res["skipped_step"] = {
+                "overflow_flag": flag, "median_ms": round(whole, 4),
+                "statistics_median_ms": round(med([a.elapsed_time(b) for a, b, _ in ev]), 4),
+                "update_exit_median_ms": round(med([b.elapsed_time(c) for _, b, c in ev]), 4),
+                "statistics_gbps": round(STATS_BYTES_PER_PARAM * n / (med([a.elapsed_time(b) for a, b, _ in ev])
+                                                                      * 1e-3) / 1e9, 1)}
+        del master, m, v, p16, gs
         torch.cuda.empty_cache()
         return res
 
@@ -327,42 +392,161 @@ def other_configs_secondary(torch, zs, tk, dev, steps):
                                  "launch-bound and cache-resident, not a roofline figure")
     out["7p5b_n64"] = reduce_step(7_500_000_000, 64, 0xC3, 1e-3 * 4096, 2.0 ** -18, 10,
                                   "7.5B at N=64: reduce of 64 slices + update (fp32 sum)")
-    out["7b_n8"] = stats_step(7_000_000_000, 8, 0xC4, 1000, "7B at N=8: statistics + update (fp16 grad)")
+    out["7b_n8"] = stats_step(7_000_000_000, 8, 0xC4, 1000, "7B at N=8: statistics + update (fp16 grad); "
+                              "skipped_step: the same with 0.001% of the gradient +inf", skip_run=True)
     out["1p5b_n1"] = stats_step(1_500_000_000, 1, 0xC5, 1,
                                 "GPT-2-XL unpartitioned (N=1): statistics + update (fp16 Student-t(3) grad, "
                                 "overflowing draws redrawn)", student=True)
     return out
 
 
-def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
-    """The oracle (single-threaded C, untuned) on the first 2^24 parameters of
-    the shard: statistics then the gated update, repeated until ~10 s."""
+class _one_core:
+    """Pins this process to one host core while the (single-threaded) oracle
+    runs, and restores the affinity afterwards."""
+
+    def __enter__(self):
+        self.allowed = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+        self.core = None
+        if self.allowed:
+            self.core = min(self.allowed)
+            os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        if self.allowed:
+            os.sched_setaffinity(0, self.allowed)
+
+
+def _repeat(fn, target_s):
+    """Calls fn() until target_s seconds have passed; (calls, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(reps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            return reps, el
+
+
+def _host_u16(torch, t):
     import numpy as np
+    return t.cpu().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _host_state(torch, master, m, v, p16):
+    return [master.cpu().numpy().copy(), m.cpu().numpy().copy(), v.cpu().numpy().copy(), _host_u16(torch, p16)]
+
+
+def cpu_baseline(torch, zs, tk, dev, g, master, m, v, p16, gpu_rates, target_s=6.0):
+    """The oracle (single-threaded C, untuned) on one pinned host core, on
+    bounded samples of the workloads, each timed for about target_s seconds
+    (the 1.5e9 flag scan once, whole):
+      gpt2xl_n4  the first 2^24 parameters of the 375,000,064 shard:
+                 statistics + update (the headline);
+      7p5b_n64   the first 2^22 rows of all 64 slices of the 117,187,584
+                 shard: the reduce alone (132 B/param), and reduce +
+                 statistics + update on the sum;
+      7b_n8      the first 2^24 parameters of the 875,000,064 shard:
+                 statistics + update;
+      1p5b_n1    one step's check of the unpartitioned run: the update of
+                 1,048,576 sampled parameters plus the statistics (flag and
+                 sum of squares) over the whole 1.5e9-value gradient.
+    gpu_rates: the GPU's params/s for the same workloads in this run (None
+    where not measured), for the ratios."""
+    import numpy as np
+
     import oracle
-    n = 1 << 24
-    g_h = g[:n].cpu().view(torch.int16).numpy().view(np.uint16).copy()
-    st = [master[:n].cpu().numpy().copy(), m[:n].cpu().numpy().copy(), v[:n].cpu().numpy().copy(),
-          p16[:n].cpu().view(torch.int16).numpy().view(np.uint16).copy()]
-    # the oracle is single-threaded: pin it to one host core while it runs
-    pinned = None
-    if hasattr(os, "sched_getaffinity"):
-        allowed = os.sched_getaffinity(0)
-        pinned = min(allowed)
-        os.sched_setaffinity(0, {pinned})
-    try:
-        reps = 0
-        t0 = time.perf_counter()
-        while True:
-            rc, _, _ = oracle.shard_adam_step(g_h, *st, step=T0 + reps, lr=LR, beta1=BETAS[0], beta2=BETAS[1],
-                                              eps=EPS, inv_scale=INV_SCALE)
+    out = {}
+    ratio = lambda a, b: round(a / b, 1) if a and b else None  # noqa: E731
+
+    # ---- inputs, prepared on the GPU with the workloads' generators (the
+    # counter-based generator gives the leading elements of each tensor)
+    n2 = 1 << 24
+    c2 = [_host_u16(torch, g[:n2]), *_host_state(torch, master[:n2], m[:n2], v[:n2], p16[:n2])]
+    n3 = 1 << 22
+    sl3 = [_host_u16(torch, tk.normal_f16_(torch.empty(n3, dtype=torch.float16, device=dev), 1e-3 * 4096, 0xC3,
+                                           tk.STREAM_GRAD + r)) for r in range(64)]
+    st3 = _host_state(torch, *tk.init_shard_state(n3, 0xC3, zero_moments=False, device=dev))
+    n4 = 1 << 24
+    g4 = _host_u16(torch, tk.normal_f16_(torch.empty(n4, dtype=torch.float16, device=dev), 1e-3 * 65536, 0xC4,
+                                         tk.STREAM_GRAD))
+    st4 = _host_state(torch, *tk.init_shard_state(n4, 0xC4, zero_moments=False, device=dev))
+    n5 = 1_500_000_000
+    g5d = tk.student_t3_f16_(torch.empty(n5, dtype=torch.float16, device=dev), 1e-3 * 65536, 0xC5, tk.STREAM_GRAD,
+                             redraw_overflow=True)
+    rng = np.random.default_rng(0xC5)
+    stride = n5 // 1_048_576
+    idx = np.arange(1_048_576, dtype=np.int64) * stride + rng.integers(0, stride, 1_048_576)
+    idx_d = torch.from_numpy(idx).to(dev)
+    m5 = tk.normal_f32_(torch.empty(n5, dtype=torch.float32, device=dev), 0.0, 0.02, 0xC5, tk.STREAM_MASTER)
+    st5 = [m5.index_select(0, idx_d).cpu().numpy().copy(), np.zeros(idx.size, np.float32),
+           np.zeros(idx.size, np.float32), np.zeros(idx.size, np.uint16)]
+    del m5
+    g5 = _host_u16(torch, g5d)
+    del g5d, idx_d
+    torch.cuda.empty_cache()
+    g5s = g5[idx].copy()
+    kw = dict(lr=LR, beta1=BETAS[0], beta2=BETAS[1], eps=EPS)
+
+    def step_fn(gh, st, t0, s):
+        def f(k):
+            rc, _, _ = oracle.shard_adam_step(gh, *st, step=t0 + k, inv_scale=s, **kw)
             assert rc == 0
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= target_s:
-                break
-    finally:
-        if pinned is not None:
-            os.sched_setaffinity(0, allowed)
+        return f
+
+    with _one_core() as pin:
+        reps, el = _repeat(step_fn(c2[0], c2[1:], T0, INV_SCALE), target_s)
+        r2 = n2 * reps / el
+        out["gpt2xl_n4"] = {"params_per_s": r2, "gbps": round(r2 * 30 / 1e9, 3),
+                            "gpu_over_oracle": ratio(gpu_rates.get("gpt2xl_n4"), r2),
+                            "sample": f"first {n2:,} params of the 375,000,064-param shard, statistics + update, "
+                                      f"{reps} repetitions in {el:.1f} s"}
+
+        def red(k):
+            oracle.grad_reduce(sl3)
+        reps, el = _repeat(red, target_s / 2)
+        rr = n3 * reps / el
+
+        def red_step(k):
+            gs = oracle.grad_reduce(sl3)
+            rc, _, _ = oracle.shard_adam_step(gs, *st3, step=10 + k, inv_scale=2.0 ** -18, **kw)
+            assert rc == 0
+        reps2, el2 = _repeat(red_step, target_s / 2)
+        rs = n3 * reps2 / el2
+        out["7p5b_n64"] = {"reduce_params_per_s": rr, "reduce_gbps": round(rr * REDUCE_BYTES_PER_PARAM(64) / 1e9, 3),
+                           "reduce_gpu_over_oracle": ratio(gpu_rates.get("7p5b_n64_reduce"), rr),
+                           "step_params_per_s": rs, "step_gbps": round(rs * (REDUCE_BYTES_PER_PARAM(64) + 30) / 1e9, 3),
+                           "step_gpu_over_oracle": ratio(gpu_rates.get("7p5b_n64_step"), rs),
+                           "sample": f"first {n3:,} rows of all 64 slices of the 117,187,584-param shard: reduce "
+                                     f"({reps} in {el:.1f} s), reduce + statistics + update on the fp32 sum "
+                                     f"({reps2} in {el2:.1f} s)"}
+        reps, el = _repeat(step_fn(g4, st4, T0, INV_SCALE), target_s)
+        r4 = n4 * reps / el
+        out["7b_n8"] = {"params_per_s": r4, "gbps": round(r4 * 30 / 1e9, 3),
+                        "gpu_over_oracle": ratio(gpu_rates.get("7b_n8"), r4),
+                        "sample": f"first {n4:,} params of the 875,000,064-param shard, statistics + update, "
+                                  f"{reps} repetitions in {el:.1f} s"}
+
+        def upd5(k):
+            assert oracle.adam_apply(g5s, *st5, step=1 + k, inv_scale=INV_SCALE, overflow=0, **kw) == 0
+        reps, el = _repeat(upd5, 1.0)
+        ru = idx.size * reps / el
+        t_scan = time.perf_counter()
+        flag, _ = oracle.grad_stats(g5, INV_SCALE)
+        t_scan = time.perf_counter() - t_scan
+        assert flag == 0
+        rscan = n5 / t_scan
+        per_step = idx.size / ru + t_scan
+        # the oracle's rate for a whole step of the 1.5e9 model (update of all
+        # parameters at the subset's rate, plus the full statistics)
+        r5 = 1.0 / (1.0 / ru + 1.0 / rscan)
+        out["1p5b_n1"] = {"subset_update_params_per_s": ru, "flag_scan_params_per_s": rscan,
+                          "flag_scan_gbps": round(rscan * 2 / 1e9, 3), "flag_scan_s": round(t_scan, 2),
+                          "per_step_check_s": round(per_step, 2), "whole_step_params_per_s": r5,
+                          "gpu_over_oracle": ratio(gpu_rates.get("1p5b_n1"), r5),
+                          "sample": f"update of {idx.size:,} stratified sampled params ({reps} in {el:.1f} s) + "
+                                    f"statistics over the whole {n5:,}-value gradient (once)"}
+        core = pin.core
     cpu_model = platform.processor() or "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -372,12 +556,12 @@ def cpu_baseline(torch, g, master, m, v, p16, target_s=10.0):
                     break
     except OSError:
         pass
-    rate = n * reps / el
-    return {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n:,} params of the 375,000,064-param shard, statistics + update, "
-                      f"{reps} repetitions in {el:.1f} s",
-            "gbps": round(rate * (UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) / 1e9, 2),
-            "pinned_core": pinned, "host_cpu": cpu_model, "host_threads": os.cpu_count()}
+    head = out["gpt2xl_n4"]
+    return {"value": head["params_per_s"], "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": head["sample"], "gbps": head["gbps"], "gpu_over_oracle": head["gpu_over_oracle"],
+            "pinned_core": core, "host_cpu": cpu_model, "host_threads": os.cpu_count(),
+            "nproc": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
+            "configs": out}
 
 
 def host_adam_secondary(torch, g, master, m, v, p16, steps=3):
@@ -430,7 +614,10 @@ def main():
     L = lay.shard_len
     log(f"workload: psi={PSI} N={N_RANKS} rank={RANK} shard_len={L}")
     master, m, v, p16 = tk.init_shard_state(L, SEED, zero_moments=False, device=dev)
-    g = tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 1e-3 * 65536, SEED, tk.STREAM_GRAD)
+    # three gradients of the workload's recipe (seeded streams), used in turn
+    grads = [tk.normal_f16_(torch.empty(L, dtype=torch.float16, device=dev), 1e-3 * 65536, SEED,
+                            tk.STREAM_GRAD + k) for k in range(N_GRAD_BUFFERS)]
+    g = grads[0]
     stats = zs.new_stats(dev)
     ws = zs.new_workspace(L, dev)
     torch.cuda.synchronize()
@@ -438,44 +625,52 @@ def main():
     ceil = ceiling(torch, tk, dev)
     log(f"ceiling: {ceil}")
 
-    def one_step(t, ev=None):
+    def one_step(t, grad, ev=None):
         layout = zs.partition_layout(PSI, N_RANKS, RANK, ALIGN)          # a1 (host)
         assert layout.shard_len == L
         if ev is not None:
             ev[2].record()
-        zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)  # a3 (2 kernels)
+        zs.grad_stats(grad, stats, inv_grad_scale=INV_SCALE, workspace=ws)  # a3 (2 kernels)
         if ev is not None:
             ev[0].record()
-        zs.adam_step(g, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
+        zs.adam_step(grad, master, m, v, p16, step=t, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
                      stats=stats, stats_precomputed=True)                # a4-a8 (1 kernel)
         if ev is not None:
             ev[1].record()
 
+    def timed_loop(t0, buffers):
+        """K steps, step k on buffers[k % len(buffers)]: wall time, and the
+        statistics and update launches timed by events on the stream."""
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(args.steps):
+            one_step(t0 + k, buffers[k % len(buffers)], evs[k])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        upd = [e[0].elapsed_time(e[1]) for e in evs]
+        sta = [e[2].elapsed_time(e[0]) for e in evs]     # statistics + finalize
+        return wall, upd, sta
+
     for i in range(args.warmup):
-        one_step(T0 + i)
+        one_step(T0 + i, grads[i % N_GRAD_BUFFERS])
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done; flag/sumsq = {zs.read_stats(stats)}")
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for k in range(args.steps):
-        one_step(T0 + args.warmup + k, evs[k])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dev_s = start.elapsed_time(end) * 1e-3
-    upd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    stats_ms = [e[2].elapsed_time(e[0]) for e in evs]     # statistics + finalize
+    wall, upd_ms, stats_ms = timed_loop(T0 + args.warmup, grads)
     stats_avg_s = sum(stats_ms) / len(stats_ms) * 1e-3
     upd_avg_s = sum(upd_ms) / len(upd_ms) * 1e-3
     upd_sorted = sorted(upd_ms)
     upd_median_ms = (upd_sorted[(len(upd_ms) - 1) // 2] + upd_sorted[len(upd_ms) // 2]) / 2
     overflow, sumsq = zs.read_stats(stats)
-    log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, device {dev_s * 1e3:.3f} ms, "
+    log(f"timed {args.steps} steps over {N_GRAD_BUFFERS} gradient buffers: wall {wall * 1e3:.3f} ms, "
         f"update avg {upd_avg_s * 1e3:.4f} ms, overflow={overflow}")
+    # the same loop with one gradient reused by every step, for comparison
+    wall1, upd1, stats1 = timed_loop(T0 + args.warmup + args.steps, [g])
+    single_buffer = {"ms_per_step": round(wall1 / args.steps * 1e3, 4), "value": L / (wall1 / args.steps),
+                     "update_avg_ms": round(sum(upd1) / len(upd1), 4),
+                     "statistics_avg_ms": round(sum(stats1) / len(stats1), 4)}
+    log(f"single gradient buffer: {single_buffer}")
 
     step_s = wall / args.steps
     value = L / step_s
@@ -483,8 +678,9 @@ def main():
     upd_gbps = UPDATE_BYTES_PER_PARAM * L / upd_avg_s / 1e9
     traffic = counter_traffic()
     stats_traffic = counter_traffic(STATS_COUNTERS_FILE)
-    # HBM bytes of the whole step from the counters (statistics + update; the
-    # 16-byte finalize is negligible), over the wall time of a step
+    # HBM bytes of the whole step from the committed counter summaries
+    # (statistics + update; the 16-byte finalize is negligible), over the
+    # wall time of a step in this run
     step_counter_bytes = traffic + stats_traffic if traffic is not None and stats_traffic is not None else None
 
     secondary = None
@@ -497,16 +693,16 @@ def main():
         clip_ms = []
         for k in range(args.steps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
+            gk = grads[k % N_GRAD_BUFFERS]
+            zs.grad_stats(gk, stats, inv_grad_scale=INV_SCALE, workspace=ws)
             a.record()
-            zs.adam_step(g, master, m, v, p16, step=T0 + 100 + k, lr=LR, betas=BETAS, eps=EPS,
+            zs.adam_step(gk, master, m, v, p16, step=T0 + 100 + k, lr=LR, betas=BETAS, eps=EPS,
                          inv_grad_scale=INV_SCALE, max_grad_norm=1.0, stats=stats, stats_precomputed=True)
             b.record()
             clip_ms.append((a, b))
         torch.cuda.synchronize()
         clip_avg = sum(a.elapsed_time(b) for a, b in clip_ms) / len(clip_ms)
-        zs.grad_stats(g, stats, inv_grad_scale=INV_SCALE, workspace=ws)
-        qwz = qwz_secondary(torch, zs, tk, dev, args.steps, g, master, m, v, p16, stats, ws, T0 + 200)
+        qwz = qwz_secondary(torch, zs, tk, dev, args.steps, grads, master, m, v, p16, stats, ws, T0 + 200)
         del ws
         secondary = {"clipped_update": {"max_grad_norm": 1.0, "avg_launch_ms": round(clip_avg, 4),
                                         "hbm_gbps": round(UPDATE_BYTES_PER_PARAM * L / (clip_avg * 1e-3) / 1e9, 1)},
@@ -520,8 +716,13 @@ def main():
     cpu = None
     host = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(torch, g, master, m, v, p16)
-        cpu["gpu_over_oracle"] = round(value / cpu["value"], 1)
+        oc = (secondary or {}).get("other_configs", {})
+        gpu_rates = {"gpt2xl_n4": value,
+                     "7p5b_n64_reduce": (secondary or {}).get("reduce_n64", {}).get("params_per_s"),
+                     "7p5b_n64_step": oc.get("7p5b_n64", {}).get("params_per_s"),
+                     "7b_n8": oc.get("7b_n8", {}).get("params_per_s"),
+                     "1p5b_n1": oc.get("1p5b_n1", {}).get("params_per_s")}
+        cpu = cpu_baseline(torch, zs, tk, dev, g, master, m, v, p16, gpu_rates)
         log(f"cpu baseline: {cpu}")
         host = host_adam_secondary(torch, g, master, m, v, p16)
         log(f"host SIMD step: {host}")
@@ -536,7 +737,14 @@ def main():
                    "psi": PSI, "n_ranks": N_RANKS, "shard_len": L, "grad_dtype": "f16",
                    "algorithmic_bytes_per_param": UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM},
         "hbm_gbps": round(whole_gbps, 1), "hbm_frac_of_peak": round(whole_gbps / PEAK_HBM_GBPS, 4),
-        "hbm_gbps_counters": (round(step_counter_bytes / step_s / 1e9, 1) if step_counter_bytes else None),
+        "gradient_buffers": N_GRAD_BUFFERS, "single_buffer": single_buffer,
+        # not measured in this run: the committed counter summaries' bytes
+        # (valid only for the kernel sources they were taken with) over this
+        # run's step time
+        "hbm_gbps_from_committed_counters": (
+            {"value": round(step_counter_bytes / step_s / 1e9, 1),
+             "files": [os.path.relpath(COUNTERS_FILE, ROOT), os.path.relpath(STATS_COUNTERS_FILE, ROOT)],
+             "kernel_source_sha256": kernel_source_hash()} if step_counter_bytes else None),
         "update_params_per_s": L / (upd_median_ms * 1e-3),
         "roofline": {"kernel": "adam_update_kernel<f16>", "bound": "hbm", "achieved": round(upd_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(upd_gbps / PEAK_HBM_GBPS, 4),
