@@ -22,7 +22,9 @@
  *     must be 16-byte aligned (ZERO_ERR_MISALIGNED otherwise).  Every array
  *     is owned by the caller; the library never allocates or frees device
  *     memory and keeps no state between calls, apart from per-device caches
- *     of the CU count and of the launch-shape LDS sizes.  Those are filled
+ *     of the CU count and of the launch-shape LDS sizes, and the fixed
+ *     32 KiB scratch array of zero_shard_adam_step_noalloc (part of the
+ *     library's code object, one copy per device).  The caches are filled
  *     by the first call of each kind on a device, with occupancy queries;
  *     make that first call outside HIP graph capture.  After it, every call
  *     enqueues kernels only (no memset, copy or allocation) and can be
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 6
+#define ZERO_SHARD_ABI_VERSION 7
 /* Largest number of simulated rank slices one reduce call accepts. */
 #define ZERO_MAX_SLICES 64
 /* Values per qwZ quantization block (one binary32 scale each). */
@@ -327,6 +329,40 @@ int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype,
                                   zero_grad_stats_t *stats,
                                   int32_t stats_precomputed, void *ws,
                                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * zero_shard_adam_step_noalloc -- zero_shard_adam_step for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It takes no workspace.  When the
+ * statistics are computed here (stats_precomputed = 0), their per-block
+ * partial results go to a scratch array the library holds in device memory:
+ * ZERO_NOALLOC_SCRATCH_BYTES (32 KiB), one copy per device, kept until the
+ * process ends.  The statistics kernel's grid is capped at 2048 blocks of
+ * one 16-byte partial each whatever the length, so that size covers every
+ * len and the call refuses none for lack of scratch (were a launch to need
+ * more, the call would return ZERO_ERR_WORKSPACE and enqueue nothing).  The
+ * call allocates nothing: on its first use on a device it looks up that
+ * device's address of the array (make that first call outside graph
+ * capture, as for every entry point), and after that it only enqueues
+ * kernels.
+ * Every call on one device uses that device's one scratch array and leaves
+ * its own partials in it.  Each call writes every partial before reading
+ * it, so nothing has to be cleared between calls, but calls that overlap in
+ * time on one device (on two streams, or from two host threads without
+ * ordering) race on the array and may produce wrong statistics, and with
+ * them a wrong skip or clipping decision: order such calls on one stream.
+ * Arguments, semantics, results and errors otherwise as
+ * zero_shard_adam_step (with stats_precomputed != 0 no scratch is used).
+ */
+#define ZERO_NOALLOC_SCRATCH_BYTES 32768
+int zero_shard_adam_step_noalloc(const void *grad, int32_t grad_dtype,
+                                 double inv_grad_scale, float *master,
+                                 float *exp_avg, float *exp_avg_sq,
+                                 uint16_t *param16, int64_t len, int64_t step,
+                                 const zero_adam_hparams_t *hp,
+                                 zero_grad_stats_t *stats,
+                                 int32_t stats_precomputed,
+                                 hipStream_t stream);
 
 /*
  * zero_qwz_quantize -- the qwZ encoder on its own ([ZS] section 5.3; [ZOS]

@@ -50,7 +50,7 @@ def test_shard_header_declares_the_path():
     assert {"zero_partition_layout", "zero_model_state_bytes", "zero_workspace_bytes",
             "zero_shard_grad_reduce", "zero_shard_grad_stats", "zero_shard_adam_step",
             "zero_shard_allgather", "zero_shard_adam_step_qwz", "zero_qwz_quantize", "zero_qwz_allgather",
-            "zero_shard_adam_step_device_t", "zero_status_string",
+            "zero_shard_adam_step_device_t", "zero_shard_adam_step_noalloc", "zero_status_string",
             "zero_last_error", "zero_shard_abi_version"} <= names
 
 
@@ -145,6 +145,38 @@ def test_adam_step_rejects_bad_arguments(kw, status):
     lib = zs.library()
     assert _adam(lib, **kw) == status
     assert lib.zero_last_error()
+
+
+def _adam_noalloc(lib, **kw):
+    a = dict(grad=A, dt=1, s=1.0, master=2 * A, m=3 * A, v=4 * A, p16=5 * A, n=100, step=1,
+             hp=_hp(), stats=6 * A, pre=0)
+    a.update(kw)
+    return lib.zero_shard_adam_step_noalloc(a["grad"], a["dt"], a["s"], a["master"], a["m"], a["v"], a["p16"],
+                                            a["n"], a["step"],
+                                            ctypes.byref(a["hp"]) if a["hp"] is not None else None,
+                                            a["stats"], a["pre"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), -1), (dict(dt=3), -1), (dict(grad=None), -1), (dict(master=None), -1),
+    (dict(stats=None), -1), (dict(hp=None), -1), (dict(step=0), -1), (dict(hp=_hp(b1=1.0)), -1),
+    (dict(s=0.0), -1), (dict(m=3 * A + 4), -2), (dict(m=2 * A + 64), -1), (dict(stats=2 * A + 96), -1),
+    (dict(stats=6 * A + 8), -2),
+    (dict(pre=1, n=-1), -1), (dict(pre=1, step=0), -1),
+])
+def test_adam_step_noalloc_rejects_bad_arguments(kw, status):
+    """The no-allocation step validates its arguments as the step does, and
+    before it looks up its scratch (so no HIP call is made here)."""
+    lib = zs.library()
+    assert _adam_noalloc(lib, **kw) == status
+    assert lib.zero_last_error()
+
+
+def test_noalloc_scratch_size_in_header():
+    text = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
+    size = int(re.search(r"#define ZERO_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1))
+    # the statistics kernel's most partials (2048) of 16 bytes each
+    assert size == zs.ZERO_NOALLOC_SCRATCH_BYTES == 2048 * 16
 
 
 def test_reduce_and_stats_reject_bad_arguments():

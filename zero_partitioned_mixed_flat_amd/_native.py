@@ -31,7 +31,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 # the version of include/zero_shard.h this binding is written against
-ZERO_SHARD_ABI_VERSION = 6
+ZERO_SHARD_ABI_VERSION = 7
 _lib.zero_shard_abi_version.argtypes = []
 _lib.zero_shard_abi_version.restype = ctypes.c_int
 if _lib.zero_shard_abi_version() != ZERO_SHARD_ABI_VERSION:
@@ -49,6 +49,7 @@ ZERO_F16 = 1
 ZERO_F32 = 2
 ZERO_MAX_SLICES = 64
 ZERO_QWZ_BLOCK = 256
+ZERO_NOALLOC_SCRATCH_BYTES = 32768
 STATS_BYTES = 16
 
 
@@ -88,6 +89,9 @@ _lib.zero_shard_adam_step_qwz.restype = ctypes.c_int
 _lib.zero_shard_adam_step_device_t.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _p, _p, _i64, _p,
                                                ctypes.POINTER(_HParams), _p, _i32, _p, _sz, _p]
 _lib.zero_shard_adam_step_device_t.restype = ctypes.c_int
+_lib.zero_shard_adam_step_noalloc.argtypes = [_p, ctypes.c_int, _dbl, _p, _p, _p, _p, _i64, _i64,
+                                              ctypes.POINTER(_HParams), _p, _i32, _p]
+_lib.zero_shard_adam_step_noalloc.restype = ctypes.c_int
 _lib.zero_qwz_quantize.argtypes = [_p, _i64, _p, _p, _p]
 _lib.zero_qwz_quantize.restype = ctypes.c_int
 _lib.zero_qwz_allgather.argtypes = [_p, _p, _i32, _i64, _i64, _p, _p]
@@ -278,6 +282,26 @@ def adam_step(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: floa
         q = [_dev_ptr(qwz_codes, torch.int8, "qwz_codes", length),
              _dev_ptr(qwz_scales, torch.float32, "qwz_scales", qwz_scales_len(length))]
         _check(_lib.zero_shard_adam_step_qwz(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, *q, *tail))
+
+
+def adam_step_noalloc(grad, master, exp_avg, exp_avg_sq, param16, *, step: int, lr: float,
+                      betas=(0.9, 0.999), eps: float = 1e-8, inv_grad_scale: float = 1.0,
+                      max_grad_norm: float = 0.0, stats, stats_precomputed: bool = False, stream=None) -> None:
+    """adam_step without a workspace: the statistics' partials go to the
+    library's static per-device scratch (zero_shard_adam_step_noalloc), so
+    the call allocates nothing.  Calls on one device must not overlap in
+    time (they share that scratch)."""
+    torch = _torch()
+    length = master.numel()
+    g_p = _dev_ptr(grad, None, "grad", length)
+    ptrs = [_dev_ptr(master, torch.float32, "master", length),
+            _dev_ptr(exp_avg, torch.float32, "exp_avg", length),
+            _dev_ptr(exp_avg_sq, torch.float32, "exp_avg_sq", length),
+            _dev_ptr(param16, torch.float16, "param16", length)]
+    hp = _HParams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(max_grad_norm))
+    _check(_lib.zero_shard_adam_step_noalloc(g_p, _grad_dtype(grad), float(inv_grad_scale), *ptrs, length,
+                                             int(step), ctypes.byref(hp), _dev_ptr(stats, None, "stats"),
+                                             int(bool(stats_precomputed)), _stream(stream)))
 
 
 def new_step_counter(device=None):

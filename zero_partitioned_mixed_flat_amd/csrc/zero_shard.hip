@@ -413,6 +413,41 @@ namespace {
 
 int64_t qwz_scales_len(int64_t len) { return ceil_div(len, zs::kQwzBlock); }
 
+// ------------------------------------------------------------------ scratch
+// The per-block partials of the statistics for zero_shard_adam_step_noalloc,
+// in the library's own device memory: one copy of this array per device,
+// held until the process ends.  The statistics kernel writes at most
+// kMaxPartials of them (its grid is capped there whatever the length), and
+// every partial the finalize reads is written earlier in the same call, so
+// nothing in it has to start at zero.  Host code never passes `scratch`
+// itself to a kernel (on the host that name is only a stand-in): it passes
+// the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = sizeof(zs::Partial) * zs::kMaxPartials;
+static __device__ __align__(256) zs::Partial scratch[zs::kMaxPartials];
+static_assert(sizeof(scratch) == kScratchBytes && kScratchBytes == ZERO_NOALLOC_SCRATCH_BYTES,
+              "scratch holds the statistics' partials");
+
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device and kept.
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ZERO_ERR_HIP, "device %d: the static scratch is kept for devices 0..%d only", dev, kMaxDevices - 1);
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(ZERO_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ZERO_OK;
+}
+
 // Capped-occupancy launch of one instantiation of the update kernel, one
 // block per tile.  Measured on the 375M shard: the plain update is fastest
 // with 1 chunk per lane at 12 blocks per CU (1.546 ms; 2 chunks at 8 blocks:
@@ -439,11 +474,18 @@ int launch_update(CapKernel cap, const void *grad, float *master, float *m, floa
 // The update, with the qwZ encoding of its fp16 output into codes and
 // scales when qwz is set, and with the step number read from (and counted
 // into) the device-resident counter when applied != NULL.
+// With use_scratch the statistics' partials go to the library's static
+// scratch instead of a caller's workspace (ws and ws_bytes are then ignored);
+// its address is looked up after every argument has been validated.
 int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scale, float *master,
                    float *exp_avg, float *exp_avg_sq, uint16_t *param16, bool qwz, int8_t *codes, float *scales,
                    int64_t len, int64_t step, zero_step_counter_t *applied, const zero_adam_hparams_t *hp,
                    zero_grad_stats_t *stats, int32_t stats_precomputed, void *ws, size_t ws_bytes,
-                   hipStream_t stream) {
+                   bool use_scratch, hipStream_t stream) {
+  if (use_scratch) {
+    ws = nullptr;
+    ws_bytes = 0;
+  }
   const bool dev_t = applied != nullptr;
   if (len < 0) return fail(ZERO_ERR_INVALID_ARG, "adam_step: len < 0");
   if (grad_dtype_in != ZERO_F16 && grad_dtype_in != ZERO_F32)
@@ -469,7 +511,7 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
   if (!aligned16(grad) || !aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
       !aligned16(param16) || !aligned16(stats) || !aligned16(codes) || !aligned16(scales))
     return fail(ZERO_ERR_MISALIGNED, "adam_step: device pointers must be 16-byte aligned");
-  if (!stats_precomputed) {
+  if (!stats_precomputed && !use_scratch) {
     if (ws == nullptr) return fail(ZERO_ERR_INVALID_ARG, "adam_step: workspace is NULL");
     if (!aligned16(ws)) return fail(ZERO_ERR_MISALIGNED, "adam_step: workspace misaligned");
     if (ws_bytes < zero_workspace_bytes(len))
@@ -510,6 +552,12 @@ int adam_step_impl(const void *grad, int32_t grad_dtype_in, double inv_grad_scal
 
   int st;
   if (!stats_precomputed) {
+    if (use_scratch) {
+      // the statistics write one partial per block, at most kMaxPartials
+      // whatever the length: exactly what the scratch holds
+      st = scratch_address(&ws);
+      if (st != ZERO_OK) return st;
+    }
     st = launch_stats(grad, grad_dtype, len, c.s, stats, ws, stream);
     if (st != ZERO_OK) return st;
   }
@@ -549,7 +597,7 @@ int zero_shard_adam_step(const void *grad, int32_t grad_dtype, double inv_grad_s
                          const zero_adam_hparams_t *hp, zero_grad_stats_t *stats, int32_t stats_precomputed,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, false, nullptr,
-                        nullptr, len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes,
+                        nullptr, len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes, false,
                         stream);
 }
 
@@ -558,7 +606,7 @@ int zero_shard_adam_step_qwz(const void *grad, int32_t grad_dtype, double inv_gr
                              int64_t len, int64_t step, const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
                              int32_t stats_precomputed, void *ws, size_t ws_bytes, hipStream_t stream) {
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, true, codes, scales,
-                        len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes,
+                        len, step, nullptr, hp, stats, stats_precomputed, ws, ws_bytes, false,
                         stream);
 }
 
@@ -572,8 +620,16 @@ int zero_shard_adam_step_device_t(const void *grad, int32_t grad_dtype, double i
     return fail(ZERO_ERR_INVALID_ARG, "adam_step_device_t: qwZ codes and scales go together");
   const bool qwz = codes != nullptr;
   return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, qwz, codes, scales,
-                        len, 1, applied_steps, hp, stats, stats_precomputed, ws, ws_bytes,
+                        len, 1, applied_steps, hp, stats, stats_precomputed, ws, ws_bytes, false,
                         stream);
+}
+
+int zero_shard_adam_step_noalloc(const void *grad, int32_t grad_dtype, double inv_grad_scale, float *master,
+                                 float *exp_avg, float *exp_avg_sq, uint16_t *param16, int64_t len, int64_t step,
+                                 const zero_adam_hparams_t *hp, zero_grad_stats_t *stats,
+                                 int32_t stats_precomputed, hipStream_t stream) {
+  return adam_step_impl(grad, grad_dtype, inv_grad_scale, master, exp_avg, exp_avg_sq, param16, false, nullptr,
+                        nullptr, len, step, nullptr, hp, stats, stats_precomputed, nullptr, 0, true, stream);
 }
 
 int zero_qwz_quantize(const uint16_t *x16, int64_t len, int8_t *codes, float *scales, hipStream_t stream) {
