@@ -509,6 +509,22 @@ def test_ceiling_kernels_compute_what_they_claim(dev):
     tk.read_f32(src, sink)
     total = float(sink.double().sum())
     assert abs(total - float(src[:body].double().sum())) <= 1e-3 * float(src[:body].abs().double().sum())
+    # the many-slice reference: every slice read (XOR over the per-block
+    # results), and with an output the per-element XOR, ragged tail included
+    ns = 1024 * 37 + 12
+    sl = [_grad16(ns, 0x78, dev, stream=tk.STREAM_GRAD + r) for r in range(7)]
+    want = np.zeros(ns, dtype=np.uint32)
+    for t in sl:
+        want ^= host_u16(t).astype(np.uint32)
+    xsink = torch.zeros(64, dtype=torch.int32, device=dev)
+    tk.read_slices(sl, xsink)
+    got = np.bitwise_xor.reduce(xsink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(want)
+    out = torch.full((ns,), -1, dtype=torch.int32, device=dev)
+    xsink.zero_()
+    tk.read_slices(sl, xsink, out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+    assert np.bitwise_xor.reduce(xsink.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(want)
 
 
 def test_explicit_stream_without_workspace(dev):

@@ -38,7 +38,8 @@
 namespace zs {
 
 constexpr int kBlock = 256;        // threads per block (statistics, folds)
-constexpr int kReduceBlock = 128;  // threads per block (reduce)
+constexpr int kReduceBlock = 64;   // threads per block (reduce): one wave
+constexpr int kReduceLane = 8;     // consecutive fp16 per lane per slice access (16 bytes)
 constexpr int kUpdateBlock = 64;   // threads per block (update): one wave
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kChunk = 4;          // consecutive elements per lane per access
@@ -213,6 +214,15 @@ __device__ __forceinline__ void block_partial(double ssq, uint32_t flag, Partial
     flag |= __shfl_xor(flag, off, kWave);
   }
   static_assert(BS % kWave == 0, "whole waves");
+  if constexpr (BS == kWave) {
+    // one wave: the butterfly already left the totals in every lane
+    if (threadIdx.x == 0) {
+      out->sumsq = ssq;
+      out->flag = flag;
+      out->pad = 0u;
+    }
+    return;
+  }
   __shared__ double s_ssq[BS / kWave];
   __shared__ uint32_t s_flag[BS / kWave];
   const int lane = threadIdx.x & (kWave - 1);
@@ -371,19 +381,20 @@ __global__ __launch_bounds__(kBlock) void fold_partials_kernel(const Partial *__
 
 // -------------------------------------------------------------------- reduce
 // Owner-side reduce of N fp16 slices into fp32, left fold in rank order,
-// optionally with the statistics of (sum * s) in the same pass.  One block
-// per tile of kReduceBlock*4*U elements (one partial per block); slices are
-// read G at a time with non-temporal loads so G*U loads are in flight before
-// the in-order adds.  The sum is written non-temporal up to element
-// keep_from and with sc1 from there on: the update that reads the sum next
-// finds that part in the Infinity Cache.
+// optionally with the statistics of (sum * s) in the same pass.  One wave
+// per tile of kReduceBlock*8*U elements (one partial per block); each lane
+// reads 8 consecutive fp16 (16 bytes) of a slice per access, slices G at a
+// time with non-temporal loads, so G*U loads are in flight before the
+// in-order adds.  The lane's 8 sums go out as two 16-byte stores.  The sum is
+// written non-temporal up to element keep_from and with sc1 from there on:
+// the update that reads the sum next finds that part in the Infinity Cache.
 template <bool WITH_STATS, int U, int G>
 __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable tab, int n, int64_t len,
                                                                    float *__restrict__ out, float s,
                                                                    Partial *__restrict__ partials,
                                                                    int64_t keep_from) {
 #pragma clang fp contract(off)
-  constexpr int kSpan = kReduceBlock * kChunk;
+  constexpr int kSpan = kReduceBlock * kReduceLane;
   constexpr int64_t kTile = static_cast<int64_t>(kSpan) * U;
   const int64_t ntiles = (len + kTile - 1) / kTile;
   double acc0 = 0.0, acc1 = 0.0;
@@ -392,28 +403,30 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
   // addresses = a tile base that is the same for the whole block (kept in
   // scalar registers) + a 32-bit lane offset; with per-lane 64-bit addresses
   // the compiler serialises the slice loads
-  const uint32_t lane = threadIdx.x * kChunk;
+  const uint32_t lane = threadIdx.x * kReduceLane;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t tbase = tile * kTile;
     if (tbase + kTile <= len) {
-      float acc[U][kChunk];
+      float acc[U][kReduceLane];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const u32x2 raw = stream_load(reinterpret_cast<const u32x2 *>(tab.p[0] + tbase + lane + k * kSpan));
-        acc[k][0] = h2f(raw.x & 0xFFFFu);
-        acc[k][1] = h2f(raw.x >> 16);
-        acc[k][2] = h2f(raw.y & 0xFFFFu);
-        acc[k][3] = h2f(raw.y >> 16);
+        const u32x4 raw = stream_load(reinterpret_cast<const u32x4 *>(tab.p[0] + tbase + lane + k * kSpan));
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[k][2 * e] = h2f(w[e] & 0xFFFFu);
+          acc[k][2 * e + 1] = h2f(w[e] >> 16);
+        }
       }
       for (int r0 = 1; r0 < n; r0 += G) {
         const int cnt = (n - r0) < G ? (n - r0) : G;
-        u32x2 raw[G][U];
+        u32x4 raw[G][U];
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           if (q < cnt) {
             const uint16_t *p = tab.p[r0 + q] + tbase;
 #pragma unroll
-            for (int k = 0; k < U; ++k) raw[q][k] = stream_load(reinterpret_cast<const u32x2 *>(p + lane + k * kSpan));
+            for (int k = 0; k < U; ++k) raw[q][k] = stream_load(reinterpret_cast<const u32x4 *>(p + lane + k * kSpan));
           }
         }
 #pragma unroll
@@ -421,10 +434,12 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
           if (q < cnt) {
 #pragma unroll
             for (int k = 0; k < U; ++k) {
-              acc[k][0] = acc[k][0] + h2f(raw[q][k].x & 0xFFFFu);
-              acc[k][1] = acc[k][1] + h2f(raw[q][k].x >> 16);
-              acc[k][2] = acc[k][2] + h2f(raw[q][k].y & 0xFFFFu);
-              acc[k][3] = acc[k][3] + h2f(raw[q][k].y >> 16);
+              const uint32_t w[4] = {raw[q][k].x, raw[q][k].y, raw[q][k].z, raw[q][k].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                acc[k][2 * e] = acc[k][2 * e] + h2f(w[e] & 0xFFFFu);
+                acc[k][2 * e + 1] = acc[k][2 * e + 1] + h2f(w[e] >> 16);
+              }
             }
           }
         }
@@ -432,16 +447,25 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
       const auto wo = store_window(out + tbase, kTile * 4);
       if (tbase >= keep_from) {
 #pragma unroll
-        for (int k = 0; k < U; ++k) window_store_as<kKeepStorePolicy>(wo, (lane + k * kSpan) * 4u, acc[k]);
+        for (int k = 0; k < U; ++k) {
+          window_store_as<kKeepStorePolicy>(wo, (lane + k * kSpan) * 4u, {acc[k][0], acc[k][1], acc[k][2], acc[k][3]});
+          window_store_as<kKeepStorePolicy>(wo, (lane + k * kSpan + 4) * 4u,
+                                            {acc[k][4], acc[k][5], acc[k][6], acc[k][7]});
+        }
       } else {
 #pragma unroll
-        for (int k = 0; k < U; ++k) window_store_as<kPlainStreamStorePolicy>(wo, (lane + k * kSpan) * 4u, acc[k]);
+        for (int k = 0; k < U; ++k) {
+          window_store_as<kPlainStreamStorePolicy>(wo, (lane + k * kSpan) * 4u,
+                                                   {acc[k][0], acc[k][1], acc[k][2], acc[k][3]});
+          window_store_as<kPlainStreamStorePolicy>(wo, (lane + k * kSpan + 4) * 4u,
+                                                   {acc[k][4], acc[k][5], acc[k][6], acc[k][7]});
+        }
       }
+      if constexpr (WITH_STATS) {
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        if constexpr (WITH_STATS) {
+        for (int k = 0; k < U; ++k) {
 #pragma unroll
-          for (int e = 0; e < kChunk; ++e) {
+          for (int e = 0; e < kReduceLane; ++e) {
             mag32 = max_mag_f32(mag32, acc[k][e]);
             if (e & 1)
               acc1 = add_sq_unscaled(acc1, acc[k][e], s);
@@ -454,7 +478,7 @@ __global__ __launch_bounds__(kReduceBlock) void grad_reduce_kernel(SliceTable ta
 #pragma unroll
       for (int k = 0; k < U; ++k) {
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
+        for (int e = 0; e < kReduceLane; ++e) {
           const int64_t j = tbase + lane + k * kSpan + e;
           if (j < len) {
             float a = h2f(tab.p[0][j]);

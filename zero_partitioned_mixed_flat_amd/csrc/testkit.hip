@@ -159,6 +159,72 @@ __global__ __launch_bounds__(kBlock) void read_f32_kernel(const f32x4 *__restric
   if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < sink_len) sink[blockIdx.x] = s[0];
 }
 
+// Many-slice streaming reference: the shape of the optimizer library's
+// owner-side reduce (tiles of 1024 elements per 128-thread block, two chunks
+// of four elements per lane, four slices' loads in flight, six blocks per
+// CU), with XOR in place of any arithmetic.
+constexpr int kSlicesMax = 64;
+struct Slices {
+  const uint16_t *p[kSlicesMax];
+};
+constexpr int kSliceBlock = 128;
+constexpr int kSliceSpan = kSliceBlock * 4;
+constexpr int64_t kSliceTile = kSliceSpan * 2;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kSliceBlock) void read_slices_kernel(Slices tab, int n, int64_t len, uint32_t *out,
+                                                                  uint32_t *sink, int sink_len) {
+  const int64_t tbase = blockIdx.x * kSliceTile;
+  const uint32_t lane = threadIdx.x * 4;
+  uint32_t w[2][2] = {{0u, 0u}, {0u, 0u}};
+  uint32_t tail = 0u;
+  if (tbase + kSliceTile <= len) {
+    for (int r0 = 0; r0 < n; r0 += 4) {
+      u32x2 raw[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (r0 + q < n) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            raw[q][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(tab.p[r0 + q] + tbase + lane + k * kSliceSpan));
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (r0 + q < n) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            w[k][0] ^= raw[q][k].x;
+            w[k][1] ^= raw[q][k].y;
+          }
+        }
+    }
+    if (out != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        __builtin_nontemporal_store(u32x4{w[k][0] & 0xFFFFu, w[k][0] >> 16, w[k][1] & 0xFFFFu, w[k][1] >> 16},
+                                    reinterpret_cast<u32x4 *>(out + tbase + lane + k * kSliceSpan));
+    }
+  } else {
+    for (int64_t j = tbase + threadIdx.x; j < len; j += kSliceBlock) {
+      uint32_t x = 0u;
+      for (int r = 0; r < n; ++r) x ^= tab.p[r][j];
+      if (out != nullptr) out[j] = x;
+      tail ^= x;
+    }
+  }
+  uint32_t x = tail ^ (w[0][0] & 0xFFFFu) ^ (w[0][0] >> 16) ^ (w[0][1] & 0xFFFFu) ^ (w[0][1] >> 16) ^
+               (w[1][0] & 0xFFFFu) ^ (w[1][0] >> 16) ^ (w[1][1] & 0xFFFFu) ^ (w[1][1] >> 16);
+  __shared__ uint32_t s[kSliceBlock];
+  s[threadIdx.x] = x;
+  __syncthreads();
+  for (int h = kSliceBlock / 2; h > 0; h >>= 1) {
+    if (static_cast<int>(threadIdx.x) < h) s[threadIdx.x] ^= s[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < sink_len) sink[blockIdx.x] = s[0];
+}
+
 int cu_count() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -258,6 +324,42 @@ int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink
   const int grid = static_cast<int>(need < 1 ? 1 : (need < cap ? need : cap));
   clear_stale_error();
   read_f32_kernel<<<grid, kBlock, 0, stream_>>>(reinterpret_cast<const f32x4 *>(src), n4, sink, sink_len);
+  return launched();
+}
+
+int zero_testkit_read_slices(const uint16_t *const *slices, int32_t n, int64_t len, uint32_t *out, uint32_t *sink,
+                             int32_t sink_len, hipStream_t stream_) {
+  if (slices == nullptr || n < 1 || n > kSlicesMax || len < 0 || len % 4 != 0 || sink == nullptr || sink_len < 1)
+    return -1;
+  if (reinterpret_cast<uintptr_t>(out) & 15u) return -1;
+  Slices tab{};
+  for (int r = 0; r < n; ++r) {
+    if ((slices[r] == nullptr && len > 0) || (reinterpret_cast<uintptr_t>(slices[r]) & 15u)) return -1;
+    tab.p[r] = slices[r];
+  }
+  const int64_t blocks = (len + kSliceTile - 1) / kSliceTile;
+  if (blocks > static_cast<int64_t>(UINT32_MAX) / kSliceBlock) return -1;
+  // six resident blocks per CU, as the reduce runs: an otherwise unused
+  // dynamic LDS allocation leaves room for no more
+  int dev = 0, lds_cu = 0, occ = 0;
+  size_t lds = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, read_slices_kernel, kSliceBlock, 0) == hipSuccess &&
+      occ > 6) {
+    for (int b = (lds_cu / 6) & ~127; b >= 128; b -= 128) {
+      int o = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, read_slices_kernel, kSliceBlock, b) != hipSuccess) break;
+      if (o == 6) {
+        lds = static_cast<size_t>(b);
+        break;
+      }
+      if (o > 6) break;
+    }
+  }
+  if (blocks == 0) return 0;
+  clear_stale_error();
+  read_slices_kernel<<<static_cast<unsigned>(blocks), kSliceBlock, lds, stream_>>>(tab, n, len, out, sink, sink_len);
   return launched();
 }
 

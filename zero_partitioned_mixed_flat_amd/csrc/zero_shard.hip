@@ -28,7 +28,7 @@ constexpr int kUpdateQwzU = 1;   // with the qwZ encoder
 constexpr int kStatsU = 8;
 constexpr int kReduceU = 2;
 constexpr int kReduceG = 4;
-constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kChunk * kReduceU;
+constexpr int64_t kReduceTile = static_cast<int64_t>(zs::kReduceBlock) * zs::kReduceLane * kReduceU;
 constexpr int kBlocksPerCU = 4;
 // Resident blocks per CU of the streaming kernels (see shard_kernels.hpp).
 constexpr int kUpdateBlocksPerCU = 12;

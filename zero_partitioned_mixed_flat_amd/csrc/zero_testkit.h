@@ -66,6 +66,18 @@ int zero_testkit_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s
 int zero_testkit_read_f32(const float *src, int64_t n, float *sink, int32_t sink_len,
                           hipStream_t stream_);
 
+/* Streaming reference of many-slice traffic: reads n (1..64) slices of
+ * len binary16 values each, in tiles of 1024 elements per 128-thread block
+ * with four slices' loads in flight and at most six blocks per CU.  When
+ * out is not NULL, out[j] (32-bit) = XOR over the slices of slices[r][j]
+ * (zero-extended), so the traffic is n*2 + 4 bytes per element; when out is
+ * NULL nothing but sink is written (n*2 bytes per element).  sink[b] for the
+ * blocks b below sink_len = XOR over block b's elements and slices of the
+ * zero-extended values.  len must be a multiple of 4 and the pointers
+ * 16-byte aligned. */
+int zero_testkit_read_slices(const uint16_t *const *slices, int32_t n, int64_t len, uint32_t *out,
+                             uint32_t *sink, int32_t sink_len, hipStream_t stream_);
+
 /* Text of the HIP error behind the last -4 on the calling thread. */
 const char *zero_testkit_last_error(void);
 

@@ -40,11 +40,12 @@ _lib.zero_testkit_student_t3_f16.argtypes = [_p, _i64, _dbl, _i32, _u64, _u32, _
 _lib.zero_testkit_inject_inf_f16.argtypes = [_p, _i64, _dbl, _u64, _u32, _p]
 _lib.zero_testkit_copy_f32.argtypes = [_p, _p, _i64, _p]
 _lib.zero_testkit_read_f32.argtypes = [_p, _i64, _p, _i32, _p]
+_lib.zero_testkit_read_slices.argtypes = [_p, _i32, _i64, _p, _p, _i32, _p]
 _lib.zero_testkit_last_error.argtypes = []
 _lib.zero_testkit_last_error.restype = ctypes.c_char_p
 for _f in ("zero_testkit_philox", "zero_testkit_normal_f32", "zero_testkit_normal_f16",
            "zero_testkit_student_t3_f16", "zero_testkit_inject_inf_f16", "zero_testkit_copy_f32",
-           "zero_testkit_read_f32"):
+           "zero_testkit_read_f32", "zero_testkit_read_slices"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 # Philox stream ids of the workload tensors
@@ -110,6 +111,19 @@ def copy_f32(src, dst):
 def read_f32(src, sink):
     _ok(_lib.zero_testkit_read_f32(src.data_ptr(), src.numel(), sink.data_ptr(), sink.numel(), _stream()),
         "read_f32")
+
+
+def read_slices(slices, sink, out=None):
+    """Streaming reference over many fp16 slices (zero_testkit_read_slices):
+    reads them all; with `out` (int32, same length) also writes the XOR of
+    the slices' values per element."""
+    import ctypes as _c
+    n = len(slices)
+    length = slices[0].numel()
+    ptrs = (_c.c_void_p * n)(*[t.data_ptr() for t in slices])
+    _ok(_lib.zero_testkit_read_slices(_c.cast(ptrs, _c.c_void_p), n, length,
+                                      out.data_ptr() if out is not None else None, sink.data_ptr(), sink.numel(),
+                                      _stream()), "read_slices")
 
 
 def init_shard_state(length: int, seed: int, *, zero_moments: bool, device="cuda"):
