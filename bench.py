@@ -142,12 +142,35 @@ def reduce_secondary(torch, zs, tk, dev, steps):
     torch.cuda.synchronize()
     sec = a.elapsed_time(b) * 1e-3 / steps
     gbps = REDUCE_BYTES_PER_PARAM(64) * n / sec / 1e9
-    del slices
+    # the access pattern's own ceilings, on the same 64 slice allocations:
+    # a plain read of all slices (128 B/param), and the same read plus a
+    # 4-byte output per element (132 B/param, the reduce's traffic)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    xout = torch.empty(n, dtype=torch.int32, device=dev)
+    ceil = {}
+    for name, fn, bytes_per in (("read64", lambda: tk.read_slices(slices, sink), 2 * 64),
+                                ("read64_write", lambda: tk.read_slices(slices, sink, xout), 2 * 64 + 4)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        cs = e0.elapsed_time(e1) * 1e-3 / steps
+        ceil[name] = {"ms": round(cs * 1e3, 4), "gbps": round(bytes_per * n / cs / 1e9, 1)}
+    del slices, xout
     return {"workload": "7.5B model at N=64: owner-side sum of 64 fp16 slices of a 117,187,584-param shard "
                         "into fp32 with fused flag/sum of squares",
             "ms": round(sec * 1e3, 4), "params_per_s": n / sec, "hbm_gbps": round(gbps, 1),
             "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_param": REDUCE_BYTES_PER_PARAM(64),
-            "traffic": counter_traffic(REDUCE_COUNTERS_FILE)}
+            "traffic": counter_traffic(REDUCE_COUNTERS_FILE),
+            "ceiling_64_slices": ceil,
+            # time of the pattern's ceilings over the reduce's time (1.0 = the
+            # reduce runs as fast as plain streaming of the same slices)
+            "frac_of_read64_write_ceiling": round(ceil["read64_write"]["ms"] / (sec * 1e3), 4),
+            "frac_of_read64_ceiling_time": round(ceil["read64"]["ms"] / (sec * 1e3), 4)}
 
 
 def allgather_secondary(torch, zs, tk, dev, steps):
