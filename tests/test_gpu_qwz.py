@@ -223,3 +223,31 @@ def test_round_trip_bound_on_device_output(dev):
     top = np.abs(codes.cpu().numpy().astype(np.int64)).reshape(-1, 256)[np.arange(blocks.shape[0]),
                                                                          blocks.argmax(1)]
     assert (top == 127).all()
+
+
+@pytest.mark.parametrize("n", [1 << 20, 777_777])
+def test_allgather_arbitrary_scales(dev, n):
+    """The decoding gather on codes and scales that need not come from this
+    encoder (uniform codes in [-127, 127], scales uniform in [1e-6, 1e-3)):
+    decode = f16(f32(code) * scale), the product rounded to binary32 first.
+    For such scales about 1 product in 20,000 lands on a binary16 tie, where
+    rounding the exact product once would differ by an ulp (a build that
+    fused the multiply and the narrowing into one instruction failed here)."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0xB3 + n)
+    shard = -(-n // 8) * 8          # the shard holds a multiple of 8 values; psi = n
+    codes = torch.randint(-127, 128, (shard,), dtype=torch.int8, device=dev, generator=gen)
+    scales = torch.rand(zs.qwz_scales_len(shard), dtype=torch.float32, device=dev, generator=gen) * 1e-3 + 1e-6
+    replica = torch.empty(n, dtype=torch.float16, device=dev)
+    zs.qwz_allgather([codes], [scales], replica)
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    ref = oracle.allgather([oracle.qwz_dequantize(c, s)], n)
+    got = host_u16(replica)
+    # the inputs do hold ties: rounding the exact product once differs there
+    exact = (c[:n].astype(np.float64) * np.repeat(s.astype(np.float64), 256)[:n]).astype(np.float16).view(np.uint16)
+    ties = int(np.count_nonzero(exact != ref))
+    bad = np.flatnonzero(got != ref)
+    say(f"  n={n}: {ties} products on a binary16 tie; {bad.size} decoded values differ")
+    assert ties > 0
+    assert bad.size == 0, f"{bad.size} differ; first at {bad[0]}: got {got[bad[0]]:#06x} want {ref[bad[0]]:#06x}"

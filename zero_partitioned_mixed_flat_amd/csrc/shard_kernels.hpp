@@ -593,8 +593,17 @@ __device__ __forceinline__ uint32_t qwz_pack(const float (&x)[kChunk], float sca
   return w;
 }
 
+// f16(code * scale): the product rounded to binary32, then to binary16.
+// The empty register constraint makes the rounded product a value of its
+// own; without it the compiler fuses the multiply and the narrowing into one
+// v_fma_mixlo_f16, which rounds the exact product once and differs from the
+// two roundings by an ulp when the binary32 product falls on a binary16 tie
+// (never for the scales max|x|/127 of fp16 blocks, about 1 value in 20,000
+// for arbitrary scales).
 __device__ __forceinline__ uint32_t qwz_decode(uint32_t code8, float scale) {
-  return f2h(static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(code8))) * scale);
+  float p = static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(code8))) * scale;
+  asm("" : "+v"(p));
+  return f2h(p);
 }
 
 // Standalone encoder and decoder: 8 values per lane (16-byte fp16 and
@@ -676,7 +685,9 @@ __global__ __launch_bounds__(kWave) void qwz_quantize_kernel(const uint16_t *__r
 
 // Receiver side of the quantized all-gather: the N owners' code and scale
 // buffers are decoded into the flat fp16 replica; block (x, y) decodes tile
-// x of shard y, only the part of the shard below psi.
+// x of shard y (and every gridDim.x-th tile after it, when the shard has more
+// tiles than one launch may have blocks), only the part of the shard below
+// psi.
 struct QwzTable {
   const uint8_t *codes[ZERO_MAX_SLICES];
   const float *scales[ZERO_MAX_SLICES];
@@ -690,32 +701,34 @@ __global__ __launch_bounds__(kWave) void qwz_allgather_kernel(QwzTable tab, int6
   const int r = blockIdx.y;
   const int64_t first = static_cast<int64_t>(r) * shard_len;
   const int64_t real = psi - first < shard_len ? psi - first : shard_len;
-  const int64_t tbase = static_cast<int64_t>(blockIdx.x) * kTile;
-  if (tbase >= real) return;
-  const uint8_t *src = tab.codes[r] + tbase;
-  const float *sc = tab.scales[r] + tbase / kQwzBlock;
-  uint16_t *dst = replica + first + tbase;
   const uint32_t lane = threadIdx.x * kQwzLane;
-  if (tbase + kTile <= real) {
-    u32x2 w[U];
-    float scale[U];
+  for (int64_t tbase = static_cast<int64_t>(blockIdx.x) * kTile; tbase < real;
+       tbase += static_cast<int64_t>(gridDim.x) * kTile) {
+    const uint8_t *src = tab.codes[r] + tbase;
+    const float *sc = tab.scales[r] + tbase / kQwzBlock;
+    uint16_t *dst = replica + first + tbase;
+    if (tbase + kTile <= real) {
+      u32x2 w[U];
+      float scale[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      w[k] = stream_load(reinterpret_cast<const u32x2 *>(src + lane + k * kRow));
-      scale[k] = sc[(lane + k * kRow) / kQwzBlock];
-    }
+      for (int k = 0; k < U; ++k) {
+        w[k] = stream_load(reinterpret_cast<const u32x2 *>(src + lane + k * kRow));
+        scale[k] = sc[(lane + k * kRow) / kQwzBlock];
+      }
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      u32x4 h;
-      h.x = qwz_decode(w[k].x, scale[k]) | (qwz_decode(w[k].x >> 8, scale[k]) << 16);
-      h.y = qwz_decode(w[k].x >> 16, scale[k]) | (qwz_decode(w[k].x >> 24, scale[k]) << 16);
-      h.z = qwz_decode(w[k].y, scale[k]) | (qwz_decode(w[k].y >> 8, scale[k]) << 16);
-      h.w = qwz_decode(w[k].y >> 16, scale[k]) | (qwz_decode(w[k].y >> 24, scale[k]) << 16);
-      stream_store(reinterpret_cast<u32x4 *>(dst + lane + k * kRow), h);
+      for (int k = 0; k < U; ++k) {
+        u32x4 h;
+        h.x = qwz_decode(w[k].x, scale[k]) | (qwz_decode(w[k].x >> 8, scale[k]) << 16);
+        h.y = qwz_decode(w[k].x >> 16, scale[k]) | (qwz_decode(w[k].x >> 24, scale[k]) << 16);
+        h.z = qwz_decode(w[k].y, scale[k]) | (qwz_decode(w[k].y >> 8, scale[k]) << 16);
+        h.w = qwz_decode(w[k].y >> 16, scale[k]) | (qwz_decode(w[k].y >> 24, scale[k]) << 16);
+        stream_store(reinterpret_cast<u32x4 *>(dst + lane + k * kRow), h);
+      }
+    } else {
+      const int64_t rem = real - tbase;
+      for (int64_t j = threadIdx.x; j < rem; j += kWave)
+        dst[j] = static_cast<uint16_t>(qwz_decode(src[j], sc[j / kQwzBlock]));
     }
-  } else {
-    const int64_t rem = real - tbase;
-    for (int64_t j = threadIdx.x; j < rem; j += kWave) dst[j] = static_cast<uint16_t>(qwz_decode(src[j], sc[j / kQwzBlock]));
   }
 }
 

@@ -683,9 +683,9 @@ int zero_qwz_allgather(const int8_t *const *codes, const float *const *scales, i
   if (psi == 0 || shard_len == 0) return ok();
   constexpr int64_t tile = static_cast<int64_t>(zs::kQwzRow) * kQwzDecU;
   const int64_t tiles = ceil_div(shard_len, tile);
-  if (tiles > INT32_MAX) return fail(ZERO_ERR_INT_OVERFLOW, "qwz_allgather: shard_len too large");
+  const int64_t gx = tiles < max_grid_x(zs::kWave) ? tiles : max_grid_x(zs::kWave);
   clear_stale_error();
-  zs::qwz_allgather_kernel<kQwzDecU><<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(n_ranks)), zs::kWave, 0,
+  zs::qwz_allgather_kernel<kQwzDecU><<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(n_ranks)), zs::kWave, 0,
                                     stream>>>(tab, shard_len, psi, replica);
   const int st = check_launch("qwz_allgather_kernel");
   return st == ZERO_OK ? ok() : st;
