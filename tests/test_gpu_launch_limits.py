@@ -24,9 +24,18 @@ SHARD = LIMIT_VALUES + 5 * 512              # five tiles beyond it
 PSI = SHARD - 100
 
 
+# the fp16 case holds the shard and its replica at once (137 GB)
+NEEDED_BYTES = 2 * 2 * SHARD + (8 << 30)
+
+
 @pytest.fixture(scope="module")
 def dev():
-    return require_gpu()
+    import torch
+    d = require_gpu()
+    total = torch.cuda.get_device_properties(d).total_memory
+    if total < NEEDED_BYTES:
+        pytest.skip(f"needs {NEEDED_BYTES / 1e9:.0f} GB of device memory, the device has {total / 1e9:.0f} GB")
+    return d
 
 
 def _regions():
