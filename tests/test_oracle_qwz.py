@@ -61,3 +61,27 @@ def test_round_trip_error_bound(orc, sigma):
         blk = np.abs(xf[b * 256:(b + 1) * 256])
         if blk.max() > 0:
             assert np.abs(codes[b * 256 + int(np.argmax(blk))]) == 127
+
+
+def test_decode_of_encoder_scales_is_the_once_rounded_product(orc):
+    """Decoding forms code * scale in binary32 and then rounds to fp16. For
+    every scale the encoder can produce (max|x|/127 of an fp16 block), that
+    equals the exact product rounded once to fp16. The check is exhaustive
+    over all positive finite fp16 maxima and all codes. The exact product
+    (at most 32 significant bits) is exact in double, and numpy narrows a
+    double to fp16 with a single rounding."""
+    maxima = np.arange(1, 0x7C00, dtype=np.uint16)          # every positive finite fp16
+    x = np.zeros((maxima.size, 256), dtype=np.uint16)
+    x[:, 0] = maxima
+    _, scales = orc.qwz_quantize(x.reshape(-1))
+    assert scales.size == maxima.size
+    codes = np.zeros((maxima.size, 256), dtype=np.int8)
+    codes[:, :255] = np.arange(-127, 128, dtype=np.int8)
+    got = orc.qwz_dequantize(codes.reshape(-1), scales).reshape(maxima.size, 256)
+    exact = codes.astype(np.float64) * scales.astype(np.float64)[:, None]
+    assert np.array_equal(got, exact.astype(np.float16).view(np.uint16))
+    # the two roundings do differ for scales the encoder never produces
+    c = np.arange(-127, 128, dtype=np.float64)
+    other = np.random.default_rng(3).uniform(1e-4, 1.0, 4000).astype(np.float32)
+    ex = c[None, :] * other.astype(np.float64)[:, None]
+    assert (ex.astype(np.float16).view(np.uint16) != ex.astype(np.float32).astype(np.float16).view(np.uint16)).any()
