@@ -651,8 +651,6 @@ def main():
     def one_step(t, grad, ev=None):
         layout = zs.partition_layout(PSI, N_RANKS, RANK, ALIGN)          # a1 (host)
         assert layout.shard_len == L
-        if ev is not None:
-            ev[2].record()
         zs.grad_stats(grad, stats, inv_grad_scale=INV_SCALE, workspace=ws)  # a3 (2 kernels)
         if ev is not None:
             ev[0].record()
@@ -662,9 +660,13 @@ def main():
             ev[1].record()
 
     def timed_loop(t0, buffers):
-        """K steps, step k on buffers[k % len(buffers)]: wall time, and the
-        statistics and update launches timed by events on the stream."""
-        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        """K steps, step k on buffers[k % len(buffers)]: wall time, the
+        update launches timed by events around them on the stream, and the
+        statistics (+ finalize and the kernel boundaries) as the time from one
+        step's update end to the next step's update start.  Each event record
+        adds about 2.5 us of stream time, so a step carries only the two
+        around its update."""
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         for k in range(args.steps):
@@ -672,7 +674,7 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         upd = [e[0].elapsed_time(e[1]) for e in evs]
-        sta = [e[2].elapsed_time(e[0]) for e in evs]     # statistics + finalize
+        sta = [evs[k - 1][1].elapsed_time(evs[k][0]) for k in range(1, len(evs))]
         return wall, upd, sta
 
     for i in range(args.warmup):
@@ -681,7 +683,7 @@ def main():
     log(f"warmup {args.warmup} steps done; flag/sumsq = {zs.read_stats(stats)}")
 
     wall, upd_ms, stats_ms = timed_loop(T0 + args.warmup, grads)
-    stats_avg_s = sum(stats_ms) / len(stats_ms) * 1e-3
+    stats_avg_s = sum(stats_ms) / len(stats_ms) * 1e-3 if stats_ms else None
     upd_avg_s = sum(upd_ms) / len(upd_ms) * 1e-3
     upd_sorted = sorted(upd_ms)
     upd_median_ms = (upd_sorted[(len(upd_ms) - 1) // 2] + upd_sorted[len(upd_ms) // 2]) / 2
@@ -692,7 +694,7 @@ def main():
     wall1, upd1, stats1 = timed_loop(T0 + args.warmup + args.steps, [g])
     single_buffer = {"ms_per_step": round(wall1 / args.steps * 1e3, 4), "value": L / (wall1 / args.steps),
                      "update_avg_ms": round(sum(upd1) / len(upd1), 4),
-                     "statistics_avg_ms": round(sum(stats1) / len(stats1), 4)}
+                     "statistics_avg_ms": round(sum(stats1) / len(stats1), 4) if stats1 else None}
     log(f"single gradient buffer: {single_buffer}")
 
     step_s = wall / args.steps
@@ -779,11 +781,13 @@ def main():
                      "rmw_ceiling_gbps": ceil.get("rmw_gbps"),
                      "frac_of_rmw_ceiling": (round(upd_gbps / ceil["rmw_gbps"], 4) if ceil.get("rmw_gbps")
                                              else None)},
-        "statistics": {"kernels": "grad_stats_kernel<f16> + finalize_stats_kernel", "bound": "hbm",
-                       "avg_ms": round(stats_avg_s * 1e3, 4),
-                       "achieved": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9, 1), "unit": "GB/s",
-                       "frac": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9 / PEAK_HBM_GBPS, 4),
-                       "traffic": stats_traffic, "algorithmic_bytes_per_launch": STATS_BYTES_PER_PARAM * L},
+        "statistics": ({"kernels": "grad_stats_kernel<f16> + finalize_stats_kernel, with the kernel boundaries "
+                                   "between one update's end and the next update's start", "bound": "hbm",
+                        "avg_ms": round(stats_avg_s * 1e3, 4),
+                        "achieved": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9, 1), "unit": "GB/s",
+                        "frac": round(STATS_BYTES_PER_PARAM * L / stats_avg_s / 1e9 / PEAK_HBM_GBPS, 4),
+                        "traffic": stats_traffic, "algorithmic_bytes_per_launch": STATS_BYTES_PER_PARAM * L}
+                       if stats_avg_s else None),
         "ceiling": ceil,
         "secondary": secondary,
         "cpu_baseline": cpu,
