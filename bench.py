@@ -587,9 +587,13 @@ def cpu_baseline(torch, zs, tk, dev, g, master, m, v, p16, gpu_rates, target_s=6
             "configs": out}
 
 
-def host_adam_secondary(torch, g, master, m, v, p16, steps=3):
+def host_adam_secondary(torch, g, master, m, v, p16, steps=5, warm=8):
     """The multi-core SIMD host step (ZeRO-Offload's CPU Adam) on the whole
-    shard in host memory: statistics + update, all OpenMP threads."""
+    shard in host memory: statistics + update, all OpenMP threads, after
+    `warm` untimed steps (a fresh allocation's first passes over host memory
+    run well below the steady rate).  Beside it, the same host's attainable
+    rate: an in-place multi-threaded read-modify-write (x += 0, 8 B/element)
+    over the master array with torch's CPU kernels."""
     import numpy as np
 
     from zero_partitioned_mixed_flat_amd import host_adam as ha
@@ -599,16 +603,27 @@ def host_adam_secondary(torch, g, master, m, v, p16, steps=3):
           p16.cpu().view(torch.int16).numpy().view(np.uint16).copy()]
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     isa = ha.set_isa(0)
-    ha.adam_step(g_h, *st, step=T0, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE, threads=threads)
+    for k in range(warm):
+        ha.adam_step(g_h, *st, step=T0 + k, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE, threads=threads)
     t0 = time.perf_counter()
     for k in range(steps):
-        ha.adam_step(g_h, *st, step=T0 + 1 + k, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
+        ha.adam_step(g_h, *st, step=T0 + warm + k, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=INV_SCALE,
                      threads=threads)
     el = (time.perf_counter() - t0) / steps
+    gbps = (UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) * n / el / 1e9
+    x = torch.from_numpy(st[0])
+    for _ in range(3):
+        x.add_(0.0)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        x.add_(0.0)
+    rmw = 8 * n / ((time.perf_counter() - t0) / steps) / 1e9
     return {"value": n / el, "unit": "params/s", "cores": threads, "kind": "host SIMD+OpenMP step",
-            "isa": ha.ISA_NAMES[isa], "ms_per_step": round(el * 1e3, 2),
-            "host_gbps": round((UPDATE_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM) * n / el / 1e9, 1),
-            "sample": f"the whole {n:,}-param shard in host memory, statistics + update, {steps} timed steps"}
+            "isa": ha.ISA_NAMES[isa], "ms_per_step": round(el * 1e3, 2), "host_gbps": round(gbps, 1),
+            "host_rmw_ceiling_gbps": round(rmw, 1), "rmw_threads": torch.get_num_threads(),
+            "frac_of_host_rmw_ceiling": round(gbps / rmw, 4),
+            "sample": f"the whole {n:,}-param shard in host memory, statistics + update, {warm} untimed and "
+                      f"{steps} timed steps"}
 
 
 def main():
