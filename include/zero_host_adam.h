@@ -74,10 +74,13 @@ typedef struct {
  *   param16     host [len] binary16 bits, written
  *   stats       host, written (or read when stats_precomputed)
  *   n_threads   OpenMP threads; 0 = the OpenMP default
+ * Each array must be aligned to its element size (2 bytes for binary16, 4
+ * for binary32), as any C array of that type is.
  * Errors: len < 0, NULL pointer (len > 0), unknown dtype, step < 1, lr < 0
  * or not finite, beta not in [0,1), eps <= 0, inv_grad_scale not finite or
- * <= 0, max_grad_norm < 0 or not finite, n_threads < 0, overlapping arrays
- * -> ZERO_HOST_ERR_INVALID_ARG; no F16C -> ZERO_HOST_ERR_UNSUPPORTED.
+ * <= 0, max_grad_norm < 0 or not finite, n_threads < 0, overlapping or
+ * misaligned arrays -> ZERO_HOST_ERR_INVALID_ARG; no F16C ->
+ * ZERO_HOST_ERR_UNSUPPORTED.
  */
 int zero_host_adam_step(const void *grad, int32_t grad_dtype,
                         double inv_grad_scale, float *master, float *exp_avg,

@@ -108,6 +108,32 @@ def test_same_bits_for_every_isa_and_thread_count():
             assert key == base, f"isa={isa} threads={threads}"
 
 
+def _p16_at(n, byte_offset):
+    """A uint16 array of n zeros starting byte_offset bytes past a 64-byte
+    boundary (odd offsets give an unaligned array)."""
+    raw = np.zeros(2 * n + 128, np.uint8)
+    start = (-raw.ctypes.data) % 64 + byte_offset
+    out = np.frombuffer(raw[start:start + 2 * n].data, dtype=np.uint16)
+    assert out.ctypes.data % 64 == byte_offset
+    return out
+
+
+@pytest.mark.parametrize("byte_offset", [0, 2, 14, 30, 62])
+@pytest.mark.parametrize("n", [5, 40, 65536 + 77])
+def test_fp16_copy_at_any_alignment(orc, byte_offset, n):
+    """The SIMD loops stream the fp16 copy with stores that need 16- or
+    32-byte alignment: the elements before the first aligned address go
+    through the scalar path."""
+    st = _state(n, 11)
+    g = _grad16(n, 11)
+    ref, _ = _oracle(orc, g, st, step=77, s=S16)
+    for isa in ISAS:
+        ha.set_isa(isa)
+        out = [a.copy() for a in st[:3]] + [_p16_at(n, byte_offset)]
+        ha.adam_step(g, *out, step=77, lr=LR, betas=BETAS, eps=EPS, inv_grad_scale=S16, threads=3)
+        assert sum(assert_state_parity(out, ref, f"isa={isa} offset={byte_offset} n={n}").values()) == 0
+
+
 @pytest.mark.parametrize("special,pos", [(np.inf, 0), (-np.inf, 65_535), (np.nan, 123_457)])
 def test_overflow_skips(orc, special, pos):
     n = 200_000
@@ -137,6 +163,19 @@ def test_clipping(orc):
     got2, stats2 = _host(g, st, step=2, s=S16, max_norm=0.05)
     assert_stats(stats2, (flag, ssq), "host clip")
     assert_state_parity(got2, ref, "host clip")
+
+
+def test_misaligned_arrays_rejected():
+    n = 64
+    st = _state(n, 12)
+    g = _grad16(n, 12)
+    with pytest.raises(ha.HostAdamError, match="aligned"):
+        ha.adam_step(g, *st[:3], _p16_at(n, 1), step=1, lr=LR)
+    raw = np.zeros(4 * n + 8, np.uint8)
+    master_odd = np.frombuffer(raw[2:2 + 4 * n].data, dtype=np.float32)
+    if master_odd.ctypes.data % 4:
+        with pytest.raises(ha.HostAdamError, match="aligned"):
+            ha.adam_step(g, master_odd, *st[1:], step=1, lr=LR)
 
 
 def test_zero_length_and_errors():
