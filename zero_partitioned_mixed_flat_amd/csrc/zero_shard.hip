@@ -35,7 +35,7 @@ constexpr int kUpdateBlocksPerCU = 12;
 constexpr int kUpdateQwzBlocksPerCU = 16;
 constexpr int kReduceBlocksPerCU = 6;
 // qwZ encoder and decoder: wave rows (512 values) per tile.
-constexpr int kQwzEncU = 8;
+constexpr int kQwzEncU = 4;
 constexpr int kQwzDecU = 1;
 // Bytes at the end of the gradient that the statistics read with the
 // default cache policy, so that the update finds them in the Infinity Cache
