@@ -340,15 +340,28 @@ __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restri
   block_partial(acc0 + acc1, flag, &partials[blockIdx.x]);
 }
 
-// Pass 2: one block folds the partials in a fixed order.
+// Pass 2: one block folds the partials in a fixed order: thread t adds
+// partials t, t + kBlock, t + 2*kBlock, ... in index order, loading eight of
+// them before adding any (one memory round trip per eight instead of one
+// each: the partials were just written by blocks on every XCD).
 __global__ __launch_bounds__(kBlock) void finalize_stats_kernel(const Partial *__restrict__ partials,
                                                                 int nparts,
                                                                 zero_grad_stats_t *__restrict__ stats) {
+  constexpr int kBatch = 8;
   double ssq = 0.0;
   uint32_t flag = 0u;
-  for (int i = threadIdx.x; i < nparts; i += kBlock) {
-    ssq += partials[i].sumsq;
-    flag |= partials[i].flag;
+  for (int base = 0; base < nparts; base += kBatch * kBlock) {
+    Partial p[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = base + k * kBlock + static_cast<int>(threadIdx.x);
+      p[k] = i < nparts ? partials[i] : Partial{0.0, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (base + k * kBlock + static_cast<int>(threadIdx.x) < nparts) ssq += p[k].sumsq;
+      flag |= p[k].flag;
+    }
   }
   __shared__ Partial total;
   block_partial(ssq, flag, &total);
