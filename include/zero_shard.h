@@ -215,10 +215,10 @@ int zero_shard_allgather(const uint16_t *const *shards, int32_t n_ranks,
  *   grad       device [len] of fp16 bit patterns (ZERO_F16) or fp32 (ZERO_F32)
  *   stats      device zero_grad_stats_t, written
  * Two kernels: per-block partials into `ws`, then one block sums them in a
- * fixed order (the result is deterministic run to run).  The gradient's
- * last 256 MiB are read so that they stay in the Infinity Cache: an update
- * enqueued right after this call reads them from there.  Errors as for the
- * reduce.
+ * fixed order (the result is deterministic run to run).  The gradient is
+ * read from its end to its start, and its first 256 MiB (read last) so that
+ * they stay in the Infinity Cache: an update enqueued right after this call
+ * starts on them and reads them from there.  Errors as for the reduce.
  */
 int zero_shard_grad_stats(const void *grad, int32_t grad_dtype,
                           int64_t len, double inv_grad_scale,

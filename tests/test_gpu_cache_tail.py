@@ -1,9 +1,10 @@
 """Arrays longer than the part that the statistics and the reduce leave in
-the Infinity Cache for the update: the statistics load the gradient's last
-256 MiB with the allocating cache policy and the rest non-temporal, and the
-reduce writes the last 256 MiB of its fp32 sum with sc1 and the rest
-non-temporal.  Both halves of each kernel run here, against the oracle, with
-a non-finite value planted on either side of the boundary in turn."""
+the Infinity Cache for the update: the statistics walk the gradient from its
+end and load its first 256 MiB with the allocating cache policy and the rest
+non-temporal, and the reduce writes the last 256 MiB of its fp32 sum with
+sc1 and the rest non-temporal.  Both halves of each kernel run here, against
+the oracle, with a non-finite value planted on either side of the boundary
+in turn."""
 import numpy as np
 import pytest
 
@@ -22,13 +23,13 @@ def dev():
 
 
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
-def test_statistics_on_both_sides_of_the_cached_tail(dev, dtype):
+def test_statistics_on_both_sides_of_the_cached_head(dev, dtype):
     import torch
     elem = 2 if dtype == "f16" else 4
-    n = TAIL_BYTES // elem + 2_891_139      # a few thousand non-temporal tiles, then the tail; ragged end
-    boundary = n - TAIL_BYTES // elem
+    n = TAIL_BYTES // elem + 2_891_139      # the cached head, then a few thousand non-temporal tiles; ragged end
+    boundary = TAIL_BYTES // elem
     s = 2.0 ** -16
-    say(f"statistics across the cached tail: {dtype}, n={n}, boundary={boundary}")
+    say(f"statistics across the cached head: {dtype}, n={n}, boundary={boundary}")
     if dtype == "f16":
         g = tk.normal_f16_(torch.empty(n, dtype=torch.float16, device=dev), 1e-3 * 65536, 0x7A, tk.STREAM_GRAD)
         host = host_u16

@@ -21,10 +21,11 @@
 //     than full occupancy;
 //   * the statistics pass uses a grid-stride loop over a grid sized from the
 //     CU count (each block leaves one partial result), with 16-byte loads, 8
-//     per lane in flight at 4 blocks per CU: non-temporal for the bulk of
-//     the gradient, cached for its last 256 MB, which the update then reads
-//     from the Infinity Cache (statistics + update 1.638 ms on the 375M
-//     shard against 1.660 ms with all loads non-temporal);
+//     per lane in flight at 4 blocks per CU, walking the gradient from its
+//     end: non-temporal for the bulk, cached for its first 256 MB, read
+//     last, which the update then reads first, from the Infinity Cache
+//     (statistics + update 1.638 ms on the 375M shard against 1.660 ms with
+//     all loads non-temporal);
 //   * reductions of the statistics: per-lane fp64 accumulation, butterfly
 //     shuffles inside the wave, LDS across the block's waves, one partial per
 //     block, then a single-block pass over the partials in index order.
@@ -259,11 +260,13 @@ __device__ __forceinline__ double add_sq_unscaled(double acc, float x, float s) 
 // ---------------------------------------------------------------- statistics
 // Pass 1 of the statistics: per-block flag and sum of squares.  Each lane
 // loads 16 bytes per access (8 fp16 or 4 fp32 values), U accesses in flight,
-// over a grid-stride loop, so the tiles are read roughly in address order.
-// Tiles from element keep_from on are loaded with the default cache policy
-// and the rest with non-temporal loads: the update that follows reads the
-// gradient again from element 0, and reaches the last tiles while their
-// lines still sit in the Infinity Cache.
+// over a grid-stride loop that walks the tiles from the last to the first.
+// Tiles below element keep_below are loaded with the default cache policy
+// and the rest with non-temporal loads: they are read last, and the update
+// that follows reads the gradient from element 0, so it starts on lines that
+// still sit in the Infinity Cache.  (Walking forward and keeping the last
+// 256 MB instead, the update reached them only at its end, after some had
+// been displaced: the step took 0.2-0.8% longer.)
 template <zero_dtype_t DT>
 constexpr int stats_per_lane() {
   return DT == ZERO_F16 ? 8 : 4;
@@ -279,7 +282,7 @@ template <zero_dtype_t DT, int U>
 __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restrict__ grad,
                                                             int64_t len, float s,
                                                             Partial *__restrict__ partials,
-                                                            int64_t keep_from) {
+                                                            int64_t keep_below) {
   constexpr int kPer = stats_per_lane<DT>();
   constexpr int kElem = DT == ZERO_F16 ? 2 : 4;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * kPer * U;
@@ -289,12 +292,12 @@ __global__ __launch_bounds__(kBlock) void grad_stats_kernel(const void *__restri
   u16x2 mag16 = {0, 0};  // running maxima of the magnitudes' bit patterns
   uint32_t mag32 = 0u;
   const uint32_t lane_bytes = threadIdx.x * 16u;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t base = tile * kTile;
+  for (int64_t step = blockIdx.x; step < ntiles; step += gridDim.x) {
+    const int64_t base = (ntiles - 1 - step) * kTile;
     if (base + kTile <= len) {
       const auto w = load_window(static_cast<const char *>(grad) + base * kElem, kTile * kElem);
       u32x4 raw[U];
-      if (base >= keep_from)
+      if (base < keep_below)
         stats_tile_load<U, kKeepLoadPolicy>(w, lane_bytes, raw);
       else
         stats_tile_load<U, kStreamLoadPolicy>(w, lane_bytes, raw);

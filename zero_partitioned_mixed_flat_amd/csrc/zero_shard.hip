@@ -37,11 +37,15 @@ constexpr int kReduceBlocksPerCU = 6;
 // qwZ encoder and decoder: wave rows (512 values) per tile.
 constexpr int kQwzEncU = 4;
 constexpr int kQwzDecU = 1;
-// Bytes at the end of the gradient that the statistics read with the
-// default cache policy, so that the update finds them in the Infinity Cache
-// (256 MB on MI355X).  Measured on the 375M shard (fp16 gradient, 750 MB):
-// statistics + update 1.638 ms with 256 MB, 1.660 ms with none, 1.641 with
-// 192 MB, 1.638-1.640 with 288-384 MB, 1.659 with the whole gradient.
+// Bytes at the start of the gradient that the statistics read (last) with
+// the default cache policy, so that the update finds them in the Infinity
+// Cache (256 MB on MI355X).  Measured on the 375M shard (fp16 gradient,
+// 750 MB), with the bytes at the end kept and read forward: statistics +
+// update 1.638 ms with 256 MB, 1.660 ms with none, 1.641 with 192 MB,
+// 1.638-1.640 with 288-384 MB, 1.659 with the whole gradient.  Read from the
+// end with the first 256 MB kept, the step took 1.673-1.675 ms against
+// 1.677-1.687 ms forward on a slower box (192 MB: 1.680-1.683, 320 MB:
+// 1.672-1.674, none: 1.700-1.703).
 constexpr int64_t kStatsKeepBytes = int64_t{256} << 20;
 // Bytes at the end of the reduce's fp32 sum written with sc1 instead of nt,
 // for the same reason.  Measured on the 7.5B / N = 64 shard (469 MB sum):
@@ -224,12 +228,12 @@ int launch_stats(const void *grad, zero_dtype_t dt, int64_t len, float s, zero_g
   const int grid = grid_for(len, tile, cus, zs::kMaxPartials);
   zs::Partial *parts = static_cast<zs::Partial *>(ws);
   const int64_t keep = kStatsKeepBytes / (dt == ZERO_F16 ? 2 : 4);
-  const int64_t keep_from = len > keep ? len - keep : 0;
+  const int64_t keep_below = len < keep ? len : keep;
   clear_stale_error();
   if (dt == ZERO_F16)
-    zs::grad_stats_kernel<ZERO_F16, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts, keep_from);
+    zs::grad_stats_kernel<ZERO_F16, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts, keep_below);
   else
-    zs::grad_stats_kernel<ZERO_F32, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts, keep_from);
+    zs::grad_stats_kernel<ZERO_F32, kStatsU><<<grid, zs::kBlock, 0, stream>>>(grad, len, s, parts, keep_below);
   st = check_launch("grad_stats_kernel");
   if (st != ZERO_OK) return st;
   return finalize(parts, grid, stats, stream);
